@@ -1,0 +1,301 @@
+"""CPU oracle for one tensor-parallel rank's shard of a Qwen3-style decoder layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library.
+
+Plain, slow, obviously-correct NumPy.  Arithmetic is float64 on the exact
+values of the bf16 (or fp32) inputs; a tensor that the GPU path stores to
+memory in bf16 is rounded to bf16 here at the same point (``store``), and
+nowhere else.
+
+Sources (web pages; sections named, not line numbers):
+  [TPS]    "Tensor parallelism from scratch", ai-infra-handbooks (anrans):
+           sections "Two ways to split", "Implementation" (tp.py: Column-/Row-
+           ParallelLinear, VocabParallelEmbedding, TPAttention, TPMLP,
+           TPTransformer), "KV heads and the limit on TP".
+  [LEDGER] "8. How several ranks share one ledger", mini-SGLang code series
+           (jaehun.me): section "Weights are cut by name" (_shard_tensor and
+           the RowParallel forward).
+  [CH9]    "Chapter 9 Multi-process and Tensor Parallelism", zero-to-sglang
+           (datawhalechina): section 3.3 "Loading Weights and Model State"
+           (shard-then-merge into qkv_proj / gate_up_proj, vocab layers).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * RMSNorm is x / sqrt(mean(x^2) + eps) * w with eps = 1e-6 (the pages import
+    RMSNorm without showing it).                        -- parity unpinned (eps)
+  * RoPE is the rotate-half form: the pair (x[i], x[i + d/2]) is rotated by the
+    angle pos * theta^(-2i/d); theta = 1e6.            -- parity unpinned (theta)
+  * Attention scale is 1/sqrt(head_dim) (the SDPA default the pages rely on).
+  * Merge order is qkv = [q; k; v] and gate_up = [gate; up] along dim 0.
+  * A vocab shard whose start passes the vocab size is empty (start clamped).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+# Weight kinds, in the order the shard rule table names them.
+W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN, W_VOCAB = range(8)
+
+
+@dataclass(frozen=True)
+class Cfg:
+    """Model shape plus this rank's place in the tensor-parallel group."""
+    hidden: int
+    intermediate: int = 0
+    n_q_heads: int = 0
+    n_kv_heads: int = 0
+    head_dim: int = 128
+    vocab: int = 0
+    tp_size: int = 1
+    tp_rank: int = 0
+    rms_eps: float = 1e-6
+    rope_theta: float = 1e6
+
+
+@dataclass(frozen=True)
+class Local:
+    lq: int           # local q heads
+    lkv: int          # local kv heads (1 when kv heads are replicated)
+    kv_head0: int     # global index of the first local kv head
+    li: int           # local intermediate size
+    n_qkv: int        # rows of the merged local qkv weight
+    vocab_start: int
+    vocab_end: int
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+def f32(x):
+    """Round float64 values to the nearest float32 (returned as float64)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16(x):
+    """Round to bfloat16 as a store does: to fp32 first, then round-to-
+    nearest-even on the upper 16 bits of the fp32 pattern.  Returns float64."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    keep = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = (keep.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return out.astype(np.float64)
+
+
+def bf16_bits(x):
+    """The uint16 bit patterns of bf16(x)."""
+    return (bf16(x).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# shard index maps   ([LEDGER] "Weights are cut by name"; [TPS] Implementation)
+# --------------------------------------------------------------------------
+
+def local_dims(c: Cfg) -> Local:
+    """Per-rank sizes.  q heads and the intermediate size are cut evenly
+    (a non-divisible head count is an error, [TPS] "KV heads and the limit on
+    TP"); kv heads are cut evenly when there are at least as many as ranks,
+    otherwise each rank keeps one whole kv head, head r*nkv//n ([LEDGER])."""
+    n, r = c.tp_size, c.tp_rank
+    if not (0 <= r < n):
+        raise ValueError("rank out of range")
+    if c.n_q_heads % n or c.intermediate % n:
+        raise ValueError("heads / intermediate not divisible by tp")
+    lq = c.n_q_heads // n
+    if c.n_q_heads == 0 and c.n_kv_heads == 0:        # vocab-only / MLP-only shape
+        lkv, kv0 = 0, 0
+    elif c.n_kv_heads >= n:
+        if c.n_kv_heads % n:
+            raise ValueError("kv heads not divisible by tp")
+        lkv, kv0 = c.n_kv_heads // n, r * (c.n_kv_heads // n)
+    else:
+        if c.n_kv_heads == 0 or n % c.n_kv_heads:
+            raise ValueError("tp not a multiple of kv heads")
+        lkv, kv0 = 1, r * c.n_kv_heads // n
+    per = -(-c.vocab // n) if c.vocab else 0           # ceil(V / n)
+    vs = min(r * per, c.vocab)
+    ve = min((r + 1) * per, c.vocab)
+    return Local(lq, lkv, kv0, c.intermediate // n, (lq + 2 * lkv) * c.head_dim, vs, ve)
+
+
+def shard_rows(c: Cfg, kind: int):
+    """(axis, start, stop) of the full [out, in] weight that rank r keeps."""
+    L = local_dims(c)
+    d, r = c.head_dim, c.tp_rank
+    if kind == W_Q:
+        return 0, r * L.lq * d, (r + 1) * L.lq * d
+    if kind in (W_K, W_V):
+        return 0, L.kv_head0 * d, (L.kv_head0 + L.lkv) * d
+    if kind in (W_GATE, W_UP):
+        return 0, r * L.li, (r + 1) * L.li
+    if kind == W_O:
+        return 1, r * L.lq * d, (r + 1) * L.lq * d
+    if kind == W_DOWN:
+        return 1, r * L.li, (r + 1) * L.li
+    if kind == W_VOCAB:
+        return 0, L.vocab_start, L.vocab_end
+    raise ValueError(kind)
+
+
+def shard(c: Cfg, kind: int, full):
+    """Rank r's slice of one full weight (column split takes rows of the
+    [out, in] matrix, row split takes columns)."""
+    axis, a, b = shard_rows(c, kind)
+    full = np.asarray(full)
+    return full[a:b, :].copy() if axis == 0 else full[:, a:b].copy()
+
+
+def merge_qkv(q, k, v):
+    """Shard first, then merge: the rank's own q/k/v slices stacked."""
+    return np.concatenate([q, k, v], axis=0)
+
+
+def merge_gate_up(g, u):
+    return np.concatenate([g, u], axis=0)
+
+
+# --------------------------------------------------------------------------
+# vocab-parallel embedding and lm head   ([TPS] Implementation; [CH9] 3.3)
+# --------------------------------------------------------------------------
+
+def embed_vocab(ids, table_local, vocab_start, vocab_end):
+    """Rows of the local table for ids inside [start, end); +0.0 rows for
+    every id outside it (including negative or >= vocab ids)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    H = table_local.shape[1]
+    out = np.zeros((ids.shape[0], H), dtype=table_local.dtype)
+    for t, i in enumerate(ids):
+        if vocab_start <= i < vocab_end:
+            out[t] = table_local[i - vocab_start]
+    return out
+
+
+def lm_head(x, table_local, store=bf16):
+    """Local slice of the logits: x @ table_local^T."""
+    return store(np.asarray(x, np.float64) @ np.asarray(table_local, np.float64).T)
+
+
+# --------------------------------------------------------------------------
+# attention block pieces   ([TPS] Implementation, TPAttention.forward)
+# --------------------------------------------------------------------------
+
+def rms_norm(v, w, eps):
+    """Normalise the last axis to unit RMS, then scale by w."""
+    v = np.asarray(v, np.float64)
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * np.asarray(w, np.float64)
+
+
+def rope_angles(positions, head_dim, theta):
+    """angle[p, i] = pos_p * theta^(-2i/d) for i < d/2."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    return np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope(v, positions, theta):
+    """Rotate-half RoPE on the last axis; v is [rows, heads, d] and
+    positions is [rows]."""
+    v = np.asarray(v, np.float64)
+    d = v.shape[-1]
+    ang = rope_angles(positions, d, theta)[:, None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = v[..., : d // 2], v[..., d // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def qkv_heads(c: Cfg, x, w_qkv_local, q_norm_w, k_norm_w, positions, store=bf16):
+    """Merged column-parallel projection, split into local heads, QK-norm
+    per head, RoPE at each row's position; returns stored (q, k, v) as
+    [rows, heads, d]."""
+    L = local_dims(c)
+    d = c.head_dim
+    y = np.asarray(x, np.float64) @ np.asarray(w_qkv_local, np.float64).T
+    q = y[:, : L.lq * d].reshape(-1, L.lq, d)
+    k = y[:, L.lq * d:(L.lq + L.lkv) * d].reshape(-1, L.lkv, d)
+    v = y[:, (L.lq + L.lkv) * d:].reshape(-1, L.lkv, d)
+    q = rope(rms_norm(q, q_norm_w, c.rms_eps), positions, c.rope_theta)
+    k = rope(rms_norm(k, k_norm_w, c.rms_eps), positions, c.rope_theta)
+    return store(q), store(k), store(v)
+
+
+def attend(q_rows, q_pos, k_seq, v_seq, rep):
+    """Causal GQA attention for a set of query rows of ONE sequence.
+
+    q_rows [n, lq, d]; q_pos [n] absolute positions; k_seq/v_seq [lkv, S, d]
+    hold the sequence's keys/values at positions 0..S-1.  Query head i reads
+    kv head i // rep; query at position p sees keys 0..p.  Returns float64
+    [n, lq, d] (unrounded)."""
+    n, lq, d = q_rows.shape
+    out = np.zeros((n, lq, d))
+    scale = 1.0 / math.sqrt(d)
+    for a in range(n):
+        p = int(q_pos[a])
+        for i in range(lq):
+            kk = k_seq[i // rep, : p + 1]
+            vv = v_seq[i // rep, : p + 1]
+            s = (kk @ q_rows[a, i]) * scale
+            s = np.exp(s - s.max())
+            out[a, i] = (s / s.sum()) @ vv
+    return out
+
+
+def qkv_attn(c: Cfg, x, B, T, past, w_qkv_local, q_norm_w, k_norm_w, w_o_local,
+             k_cache, v_cache, store=bf16):
+    """One call of the attention shard: B sequences with T new tokens each at
+    positions past..past+T-1.  Writes k/v into copies of the caches
+    [B, lkv, S_max, d] and returns dict(q, k_cache, v_cache, attn, partial),
+    q/attn as [B*T, lq*d] and the row-parallel partial [B*T, H]."""
+    L = local_dims(c)
+    d = c.head_dim
+    rep = L.lq // L.lkv
+    x = np.asarray(x, np.float64)
+    pos = np.tile(np.arange(past, past + T), B)
+    q, k, v = qkv_heads(c, x, w_qkv_local, q_norm_w, k_norm_w, pos, store)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    attn = np.zeros((B * T, L.lq, d))
+    for b in range(B):
+        rows = slice(b * T, (b + 1) * T)
+        kc[b, :, past:past + T] = k[rows].transpose(1, 0, 2)
+        vc[b, :, past:past + T] = v[rows].transpose(1, 0, 2)
+        attn[rows] = attend(q[rows], pos[rows], kc[b, :, : past + T], vc[b, :, : past + T], rep)
+    attn = store(attn.reshape(B * T, L.lq * d))
+    partial = store(attn @ np.asarray(w_o_local, np.float64).T)
+    return dict(q=q.reshape(B * T, L.lq * d), k_cache=kc, v_cache=vc, attn=attn, partial=partial)
+
+
+# --------------------------------------------------------------------------
+# MLP shard   ([TPS] Implementation, TPMLP.forward)
+# --------------------------------------------------------------------------
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def mlp(c: Cfg, x, w_gate_up_local, w_down_local, store=bf16):
+    """h = silu(x Wg^T) * (x Wu^T) on the local intermediate slice, then the
+    row-parallel partial h Wd^T.  Returns (h, partial), both stored."""
+    li = local_dims(c).li
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w_gate_up_local, np.float64)
+    g = x @ w[:li].T
+    u = x @ w[li:].T
+    h = store(silu(g) * u)
+    return h, store(h @ np.asarray(w_down_local, np.float64).T)
+
+
+# --------------------------------------------------------------------------
+# unsharded reference = the same maths at tp = 1
+# --------------------------------------------------------------------------
+
+def unsharded(c: Cfg) -> Cfg:
+    return Cfg(c.hidden, c.intermediate, c.n_q_heads, c.n_kv_heads, c.head_dim, c.vocab,
+               1, 0, c.rms_eps, c.rope_theta)
+
+
+def with_rank(c: Cfg, r: int) -> Cfg:
+    return Cfg(c.hidden, c.intermediate, c.n_q_heads, c.n_kv_heads, c.head_dim, c.vocab,
+               c.tp_size, r, c.rms_eps, c.rope_theta)
