@@ -1,0 +1,211 @@
+/*
+ * tpshard.h -- C ABI of the tensor-parallel rank shard library (libtpshard.so).
+ *
+ * One tensor-parallel rank's shard of a Qwen3-style decoder layer on one
+ * MI355X (gfx950):
+ *   - the merged column-parallel QKV and gate_up projections,
+ *   - SiLU(gate) * up,
+ *   - the row-parallel o_proj / down_proj, which leave partial sums,
+ *   - GQA attention over the rank's local heads (kv heads replicated when the
+ *     tensor-parallel size exceeds the kv-head count),
+ *   - the vocab-parallel masked embedding and the lm_head vocab slice.
+ *
+ * Sources (web pages; the section that defines each operation is cited at
+ * each entry point):
+ *   [TPS]    "Tensor parallelism from scratch" (ai-infra-handbooks):
+ *            "Two ways to split", "Implementation", "KV heads and the limit
+ *            on TP".
+ *   [LEDGER] "8. How several ranks share one ledger" (mini-SGLang series):
+ *            "Weights are cut by name".
+ *   [CH9]    "Chapter 9 Multi-process and Tensor Parallelism"
+ *            (zero-to-sglang): 3.3 "Loading Weights and Model State".
+ *
+ * Conventions for every entry point
+ *   - All tensors are caller-owned, contiguous, row-major device memory
+ *     (allocated with hipMalloc or by PyTorch).  The library allocates
+ *     nothing and keeps no global state; calls are re-entrant.
+ *   - Weights use the [out, in] layout of a linear layer (the input dimension
+ *     is contiguous).  Element type is cfg->dtype: TP_BF16 (bfloat16 bits)
+ *     or TP_F32.
+ *   - Every pointer argument must be 16-byte aligned (TP_ERR_ALIGN).
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     non-zero return nothing has been written.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and runs
+ *     asynchronously; TP_ERR_LAUNCH reports a failed launch.
+ *   - Collectives are not part of the library: a row-parallel call returns
+ *     the rank's partial sum, a column-parallel call the rank's slice.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = -1,      /* a required pointer is NULL                        */
+  TP_ERR_RANK = -2,      /* tp_rank outside [0, tp_size) or tp_size < 1       */
+  TP_ERR_SHAPE = -3,     /* heads / intermediate / vocab not splittable, or a
+                            size the kernels do not support                   */
+  TP_ERR_DTYPE = -4,     /* dtype not supported by this entry point           */
+  TP_ERR_ALIGN = -5,     /* pointer not 16-byte aligned                       */
+  TP_ERR_WORKSPACE = -6, /* workspace smaller than tp_workspace_bytes()       */
+  TP_ERR_RANGE = -7,     /* negative size, or past_len + T > S_max            */
+  TP_ERR_LAUNCH = -8,    /* a kernel launch failed                            */
+  TP_ERR_KIND = -9       /* unknown tp_weight_kind / tp_op                    */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Weight names of the shard rule table ([LEDGER] "Weights are cut by name"). */
+typedef enum {
+  TP_W_Q = 0, TP_W_K = 1, TP_W_V = 2, TP_W_O = 3,
+  TP_W_GATE = 4, TP_W_UP = 5, TP_W_DOWN = 6, TP_W_VOCAB = 7
+} tp_weight_kind;
+
+typedef enum { TP_OP_ATTN = 0, TP_OP_MLP = 1 } tp_op;
+
+/* Model shape and this rank's place in the group ([TPS] "Implementation":
+ * every layer is built from the rank and the group size).  48 bytes. */
+typedef struct {
+  int32_t hidden;        /* H                                                 */
+  int32_t intermediate;  /* I (full, unsharded)                               */
+  int32_t n_q_heads;     /* full q-head count                                 */
+  int32_t n_kv_heads;    /* full kv-head count                                */
+  int32_t head_dim;      /* d                                                 */
+  int32_t tp_size;       /* n                                                 */
+  int32_t tp_rank;       /* r                                                 */
+  int32_t dtype;         /* tp_dtype                                          */
+  int64_t vocab;         /* V (full)                                          */
+  float rms_eps;         /* QK-norm epsilon (Qwen3: 1e-6)                     */
+  float rope_theta;      /* RoPE base (Qwen3: 1e6)                            */
+} tp_cfg;
+
+/* Per-rank sizes ([LEDGER] "Weights are cut by name"; [TPS] "KV heads and
+ * the limit on TP"). */
+typedef struct {
+  int32_t lq;            /* local q heads = n_q_heads / n                     */
+  int32_t lkv;           /* local kv heads = n_kv_heads / n, or 1 when
+                            n_kv_heads < n (replicated)                        */
+  int32_t kv_head0;      /* global index of the first local kv head:
+                            r * lkv, or r * n_kv_heads / n when replicated     */
+  int32_t li;            /* local intermediate = I / n                        */
+  int64_t n_qkv;         /* rows of the merged local qkv weight (lq+2lkv)*d  */
+  int64_t vocab_start;   /* local vocab rows [vocab_start, vocab_end):        */
+  int64_t vocab_end;     /* per = ceil(V/n), [min(r*per,V), min((r+1)*per,V)) */
+} tp_local;
+
+/* ------------------------------------------------------------------------
+ * Host-only helpers: no HIP calls, usable on a machine without a GPU.
+ * ---------------------------------------------------------------------- */
+
+/* Validates cfg and fills *out.  Rejected ([TPS] "KV heads and the limit on
+ * TP": a head count that does not divide is an error):
+ *   tp_rank outside [0, tp_size)                      -> TP_ERR_RANK
+ *   n_q_heads % n, intermediate % n                   -> TP_ERR_SHAPE
+ *   n_kv_heads >= n and n_kv_heads % n                -> TP_ERR_SHAPE
+ *   n_kv_heads <  n and n % n_kv_heads                -> TP_ERR_SHAPE
+ *   negative sizes, dtype not TP_F32/TP_BF16          -> TP_ERR_SHAPE / DTYPE
+ * A shape with no heads (n_q_heads = n_kv_heads = 0) is valid for the MLP,
+ * embedding and lm_head entry points. */
+int tp_local_dims(const tp_cfg* cfg, tp_local* out);
+
+/* Bytes of device workspace that tp_qkv_attn (op = TP_OP_ATTN) or tp_mlp
+ * (op = TP_OP_MLP) needs for B sequences of T new tokens after past_len
+ * cached ones (tp_mlp: M = B * T rows; past_len ignored). */
+int tp_workspace_bytes(const tp_cfg* cfg, int op, int64_t B, int64_t T, int64_t past_len,
+                       size_t* out_bytes);
+
+/* Static description of a status code. */
+const char* tp_status_str(int status);
+
+/* ------------------------------------------------------------------------
+ * Device entry points
+ * ---------------------------------------------------------------------- */
+
+/* tp_shard_weights -- copy rank r's shard of one full weight into its place
+ * in the rank's local (merged) weight ([LEDGER] "Weights are cut by name":
+ * the shard rule table; [CH9] 3.3: shard first, then merge q/k/v into
+ * qkv_proj and gate/up into gate_up_proj).  A bit-exact copy.
+ *   kind     full (unsharded, [out, in])   dst and the rows this call writes
+ *   TP_W_Q     [nq*d,  H]  rows r*lq*d..    qkv [n_qkv, H], rows [0, lq*d)
+ *   TP_W_K     [nkv*d, H]  kv heads         qkv, rows [lq*d, (lq+lkv)*d)
+ *   TP_W_V     [nkv*d, H]  kv_head0..+lkv   qkv, rows [(lq+lkv)*d, n_qkv)
+ *   TP_W_GATE  [I, H]      rows r*li..      gate_up [2*li, H], rows [0, li)
+ *   TP_W_UP    [I, H]      rows r*li..      gate_up, rows [li, 2*li)
+ *   TP_W_O     [H, nq*d]   cols r*lq*d..    o_local [H, lq*d] (whole)
+ *   TP_W_DOWN  [H, I]      cols r*li..      down_local [H, li] (whole)
+ *   TP_W_VOCAB [V, H]      rows vocab_start.. vocab_local [vocab_end-vocab_start, H]
+ * When n_kv_heads < n the K/V shard is the single head kv_head0 (replica).
+ * Elements are 2 (TP_BF16) or 4 (TP_F32) bytes. */
+int tp_shard_weights(const tp_cfg* cfg, int kind, const void* full, void* dst, void* stream);
+
+/* tp_embed_vocab -- vocab-parallel embedding lookup before its all-reduce
+ * ([TPS] "Implementation", VocabParallelEmbedding; [CH9] 3.3 vocab layers):
+ *   out[t, :] = vocab_local[ids[t] - vocab_start, :]  if vocab_start <= ids[t] < vocab_end
+ *             = +0.0                                  otherwise (any id, incl. negative)
+ * ids: int32 [n_tokens]; vocab_local: [vocab_end - vocab_start, H];
+ * out: [n_tokens, H].  Bit-exact copy.  n_tokens = 0 is a no-op. */
+int tp_embed_vocab(const tp_cfg* cfg, const int32_t* ids, int64_t n_tokens,
+                   const void* vocab_local, void* out, void* stream);
+
+/* tp_qkv_attn -- the attention half of the layer shard ([TPS]
+ * "Implementation", TPAttention.forward; "Two ways to split"):
+ *   qkv = x @ w_qkv^T            merged column-parallel projection
+ *   q, k, v = split into lq, lkv, lkv heads of d
+ *   q, k = RMSNorm_d(q) * q_norm_w, RMSNorm_d(k) * k_norm_w   (QK-norm)
+ *   q, k = RoPE(q, pos), RoPE(k, pos)   rotate-half, pos = past_len + t
+ *   cache[b, h, past_len + t, :] = k, v
+ *   attn = softmax(q k^T / sqrt(d) + causal) v, q head i reads kv head i/rep
+ *   out_partial = attn @ w_o^T   row-parallel partial (before its all-reduce)
+ * Arguments:
+ *   x          bf16 [B*T, H], the normed hidden states (row b*T + t)
+ *   w_qkv      bf16 [n_qkv, H] merged local weight ([q; k; v])
+ *   q_norm_w, k_norm_w  bf16 [d]
+ *   w_o        bf16 [H, lq*d] local o_proj (column slice)
+ *   k_cache, v_cache    bf16 [B, lkv, S_max, d]; positions < past_len are
+ *              read, [past_len, past_len+T) written, the rest untouched
+ *   q_out_opt  bf16 [B*T, lq*d] normed+rotated q, or NULL
+ *   attn_out_opt bf16 [B*T, lq*d] attention output, or NULL
+ *   out_partial  bf16 [B*T, H]
+ *   workspace  >= tp_workspace_bytes(cfg, TP_OP_ATTN, B, T, past_len)
+ * Requires dtype TP_BF16 (TP_ERR_DTYPE), head_dim == 128 and H % 8 == 0
+ * (TP_ERR_SHAPE), past_len >= 0, past_len + T <= S_max (TP_ERR_RANGE).
+ * B*T = 0 is a no-op. */
+int tp_qkv_attn(const tp_cfg* cfg, const void* x, int32_t B, int32_t T, int32_t past_len,
+                const void* w_qkv, const void* q_norm_w, const void* k_norm_w, const void* w_o,
+                void* k_cache, void* v_cache, int32_t S_max,
+                void* q_out_opt, void* attn_out_opt, void* out_partial,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/* tp_mlp -- the MLP half of the layer shard ([TPS] "Implementation",
+ * TPMLP.forward; "Two ways to split": gate/up column split, down row split):
+ *   h = silu(x @ w_gate^T) * (x @ w_up^T),  silu(z) = z / (1 + exp(-z))
+ *   out_partial = h @ w_down^T   (partial sum before the all-reduce)
+ * x: [M, H]; w_gate_up: [2*li, H] merged ([gate; up]); w_down: [H, li];
+ * h_opt: [M, li] or NULL; out_partial: [M, H].  TP_BF16 (fp32 accumulate,
+ * bf16 stores) or TP_F32.  H and li must be multiples of 8 (TP_ERR_SHAPE).
+ * workspace >= tp_workspace_bytes(cfg, TP_OP_MLP, M, 1, 0).  M = 0: no-op. */
+int tp_mlp(const tp_cfg* cfg, const void* x, int64_t M, const void* w_gate_up,
+           const void* w_down, void* h_opt, void* out_partial,
+           void* workspace, size_t ws_bytes, void* stream);
+
+/* tp_lm_head -- the rank's slice of the logits before the all-gather ([CH9]
+ * 3.3 ParallelLMHead; [TPS] "Implementation", the vocab-split output layer,
+ * tied to the embedding shard when the model ties them):
+ *   logits_local = x @ vocab_local^T
+ * x: [M, H]; vocab_local: [vocab_end - vocab_start, H];
+ * logits_local: [M, vocab_end - vocab_start].  Which rows to run (e.g. only
+ * each sequence's last token) is the caller's choice.  M = 0: no-op. */
+int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local,
+               void* logits_local, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

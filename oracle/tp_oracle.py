@@ -206,19 +206,34 @@ def rope(v, positions, theta):
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def qkv_heads(c: Cfg, x, w_qkv_local, q_norm_w, k_norm_w, positions, store=bf16):
-    """Merged column-parallel projection, split into local heads, QK-norm
-    per head, RoPE at each row's position; returns stored (q, k, v) as
-    [rows, heads, d]."""
+def q_heads(c: Cfg, x, w_qkv_local, q_norm_w, positions, store=bf16):
+    """q part of the merged column-parallel projection: the rank's lq heads,
+    QK-norm per head, then RoPE at each row's position; [rows, lq, d]."""
     L = local_dims(c)
     d = c.head_dim
-    y = np.asarray(x, np.float64) @ np.asarray(w_qkv_local, np.float64).T
-    q = y[:, : L.lq * d].reshape(-1, L.lq, d)
-    k = y[:, L.lq * d:(L.lq + L.lkv) * d].reshape(-1, L.lkv, d)
-    v = y[:, (L.lq + L.lkv) * d:].reshape(-1, L.lkv, d)
-    q = rope(rms_norm(q, q_norm_w, c.rms_eps), positions, c.rope_theta)
+    w = np.asarray(w_qkv_local, np.float64)[: L.lq * d]
+    q = (np.asarray(x, np.float64) @ w.T).reshape(-1, L.lq, d)
+    return store(rope(rms_norm(q, q_norm_w, c.rms_eps), positions, c.rope_theta))
+
+
+def kv_heads(c: Cfg, x, w_qkv_local, k_norm_w, positions, store=bf16):
+    """k and v parts of the merged projection: k gets QK-norm and RoPE, v
+    neither; each [rows, lkv, d]."""
+    L = local_dims(c)
+    d = c.head_dim
+    w = np.asarray(w_qkv_local, np.float64)
+    x = np.asarray(x, np.float64)
+    k = (x @ w[L.lq * d:(L.lq + L.lkv) * d].T).reshape(-1, L.lkv, d)
+    v = (x @ w[(L.lq + L.lkv) * d:].T).reshape(-1, L.lkv, d)
     k = rope(rms_norm(k, k_norm_w, c.rms_eps), positions, c.rope_theta)
-    return store(q), store(k), store(v)
+    return store(k), store(v)
+
+
+def qkv_heads(c: Cfg, x, w_qkv_local, q_norm_w, k_norm_w, positions, store=bf16):
+    """Merged column-parallel projection split into the rank's heads:
+    stored (q, k, v) as [rows, heads, d]."""
+    k, v = kv_heads(c, x, w_qkv_local, k_norm_w, positions, store)
+    return q_heads(c, x, w_qkv_local, q_norm_w, positions, store), k, v
 
 
 def attend(q_rows, q_pos, k_seq, v_seq, rep):

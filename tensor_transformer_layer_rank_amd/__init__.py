@@ -1,0 +1,153 @@
+"""Python binding of libtpshard (one tensor-parallel rank's shard of a
+Qwen3-style decoder layer on MI355X).  Argument marshalling only: every step
+of the computation runs in the HIP kernels behind the C ABI (include/tpshard.h).
+
+Tensors are torch tensors on the GPU (device memory and streams only); each
+call is enqueued on torch's current stream.  A non-zero status from the
+library raises TpError.  If the shared library is not built, importing the
+binding works but every call raises (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpshard.so")
+
+TP_F32, TP_BF16 = 0, 1
+TP_W_Q, TP_W_K, TP_W_V, TP_W_O, TP_W_GATE, TP_W_UP, TP_W_DOWN, TP_W_VOCAB = range(8)
+TP_OP_ATTN, TP_OP_MLP = 0, 1
+
+EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_shard_weights", "tp_embed_vocab",
+           "tp_qkv_attn", "tp_mlp", "tp_lm_head")
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class tp_cfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("tp_size", ctypes.c_int32),
+                ("tp_rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("vocab", ctypes.c_int64),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+
+class tp_local(ctypes.Structure):
+    _fields_ = [("lq", ctypes.c_int32), ("lkv", ctypes.c_int32), ("kv_head0", ctypes.c_int32),
+                ("li", ctypes.c_int32), ("n_qkv", ctypes.c_int64), ("vocab_start", ctypes.c_int64),
+                ("vocab_end", ctypes.c_int64)]
+
+
+@dataclass
+class Cfg:
+    """Model shape and rank (mirrors tp_cfg)."""
+    hidden: int
+    intermediate: int = 0
+    n_q_heads: int = 0
+    n_kv_heads: int = 0
+    head_dim: int = 128
+    tp_size: int = 1
+    tp_rank: int = 0
+    dtype: int = TP_BF16
+    vocab: int = 0
+    rms_eps: float = 1e-6
+    rope_theta: float = 1e6
+
+    def c(self) -> tp_cfg:
+        return tp_cfg(self.hidden, self.intermediate, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                      self.tp_size, self.tp_rank, self.dtype, self.vocab, self.rms_eps, self.rope_theta)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m tensor_transformer_layer_rank_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        C = ctypes.POINTER(tp_cfg)
+        L.tp_local_dims.argtypes = [C, ctypes.POINTER(tp_local)]
+        L.tp_workspace_bytes.argtypes = [C, ctypes.c_int, I64, I64, I64, ctypes.POINTER(SZ)]
+        L.tp_status_str.argtypes = [ctypes.c_int]
+        L.tp_status_str.restype = ctypes.c_char_p
+        L.tp_shard_weights.argtypes = [C, ctypes.c_int, P, P, P]
+        L.tp_embed_vocab.argtypes = [C, P, I64, P, P, P]
+        L.tp_qkv_attn.argtypes = [C, P, I32, I32, I32, P, P, P, P, P, P, I32, P, P, P, P, SZ, P]
+        L.tp_mlp.argtypes = [C, P, I64, P, P, P, P, P, SZ, P]
+        L.tp_lm_head.argtypes = [C, P, I64, P, P, P]
+        for name in EXPORTS:
+            if name != "tp_status_str":
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(st: int):
+    if st != 0:
+        raise TpError(st, lib().tp_status_str(st).decode())
+
+
+def _ptr(t):
+    """Device pointer of a tensor, or NULL for None (no copies, no checks:
+    shapes and dtypes are the caller's contract, see tpshard.h)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def tp_local_dims(cfg: Cfg) -> tp_local:
+    out = tp_local()
+    _check(lib().tp_local_dims(ctypes.byref(cfg.c()), ctypes.byref(out)))
+    return out
+
+
+def tp_workspace_bytes(cfg: Cfg, op: int, B: int, T: int, past_len: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tp_workspace_bytes(ctypes.byref(cfg.c()), op, B, T, past_len, ctypes.byref(n)))
+    return n.value
+
+
+def tp_status_str(status: int) -> str:
+    return lib().tp_status_str(status).decode()
+
+
+def tp_shard_weights(cfg: Cfg, kind: int, full, dst, stream=None):
+    _check(lib().tp_shard_weights(ctypes.byref(cfg.c()), kind, _ptr(full), _ptr(dst), _stream(stream)))
+
+
+def tp_embed_vocab(cfg: Cfg, ids, vocab_local, out, stream=None):
+    _check(lib().tp_embed_vocab(ctypes.byref(cfg.c()), _ptr(ids), ids.numel(), _ptr(vocab_local), _ptr(out),
+                                _stream(stream)))
+
+
+def tp_qkv_attn(cfg: Cfg, x, B: int, T: int, past_len: int, w_qkv, q_norm_w, k_norm_w, w_o, k_cache, v_cache,
+                S_max: int, out_partial, workspace, q_out=None, attn_out=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tp_qkv_attn(ctypes.byref(cfg.c()), _ptr(x), B, T, past_len, _ptr(w_qkv), _ptr(q_norm_w),
+                             _ptr(k_norm_w), _ptr(w_o), _ptr(k_cache), _ptr(v_cache), S_max, _ptr(q_out),
+                             _ptr(attn_out), _ptr(out_partial), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_mlp(cfg: Cfg, x, M: int, w_gate_up, w_down, out_partial, workspace, h_out=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tp_mlp(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(w_gate_up), _ptr(w_down), _ptr(h_out),
+                        _ptr(out_partial), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_lm_head(cfg: Cfg, x, M: int, vocab_local, logits_local, stream=None):
+    _check(lib().tp_lm_head(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(vocab_local), _ptr(logits_local),
+                            _stream(stream)))

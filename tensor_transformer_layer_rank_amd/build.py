@@ -1,0 +1,75 @@
+"""Builds libtpshard.so (HIP, gfx950) in-tree from csrc/.
+
+    python -m tensor_transformer_layer_rank_amd.build [-j N] [--asm]
+
+Objects go to _build/ at the repository root; the shared library is written
+next to this file, where the binding loads it.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libtpshard.so")
+ARCH = "gfx950"
+
+SOURCES = ["tpshard.cpp", "copy_kernels.hip", "gemm.hip", "qkv_epilogue.hip", "attn_decode.hip",
+           "attn_prefill.hip"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libtpshard)")
+
+
+FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Wno-unused-function", "-Wno-unused-variable",
+         # packed-fp32 VALU forms are kept out of the generated code
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def _compile(src: str, asm: bool) -> str:
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
+    if err.strip():
+        print(err, file=sys.stderr)
+    if asm:
+        s = os.path.join(BUILD, src + ".s")
+        subprocess.run([hipcc(), *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", s],
+                       capture_output=True, text=True, check=True)
+    return obj
+
+
+def build(jobs: int = 0, asm: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, asm), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-j", type=int, default=0)
+    ap.add_argument("--asm", action="store_true", help="also write device assembly to _build/")
+    a = ap.parse_args()
+    print(build(a.j, a.asm))

@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP translation units of libtpshard.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 32x32x16, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace tps {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+__device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // RNE (v_cvt_pk_bf16_f32)
+
+// --- GEMM -----------------------------------------------------------------
+// C[M, N] = A[M, K] * B[N, K]^T, A and B bf16 with K contiguous, fp32
+// accumulation.  Epilogues:
+enum GemmEpi {
+  EPI_BF16 = 0,      // C bf16 [M, N] (row stride ldc)
+  EPI_F32 = 1,       // C fp32 [M, N]; with split-K: partials [splits, M, N]
+  EPI_SILU_BF16 = 2  // B = [gate; up] with `li` rows each; C = silu(gate)*up, bf16 [M, li]
+};
+
+struct GemmProblem {
+  const bf16* A;
+  const bf16* B;
+  void* C;
+  int64_t M, N, K;      // N = rows of B (for EPI_SILU_BF16: 2*li)
+  int64_t lda, ldb, ldc;
+  int64_t li;           // EPI_SILU_BF16 only
+};
+
+// Chooses a tile shape and launches.  When the grid would not fill the GPU
+// and `scratch` holds at least gemm_scratch_bytes() for the same problem,
+// K is split and fp32 partials in scratch are summed by a second kernel;
+// otherwise (scratch NULL or too small) no split is made.
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int epi);
+hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratch_bytes, hipStream_t s);
+
+// fp32 GEMM (small problems): C = A B^T, or silu-mul of the gate/up halves.
+hipError_t gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K,
+                    int silu_li, hipStream_t s);
+
+// --- copies ---------------------------------------------------------------
+// dst[r, c] = src[(row0 + r) * src_ld + col0 + c] for r < rows, c < cols
+// (elements of `esize` bytes); dst row stride dst_ld.
+hipError_t copy2d(const void* src, int64_t src_ld, int64_t row0, int64_t col0, void* dst,
+                  int64_t dst_ld, int64_t rows, int64_t cols, int esize, hipStream_t s);
+
+hipError_t embed_masked(const int32_t* ids, int64_t n, const void* table, int64_t vstart,
+                        int64_t vend, int64_t H, int esize, void* out, hipStream_t s);
+
+// --- attention block ------------------------------------------------------
+struct QkvArgs {
+  const float* qkv;      // [M, n_qkv] fp32 projection output
+  const bf16* q_norm_w;  // [128]
+  const bf16* k_norm_w;  // [128]
+  bf16* q_out;           // [M, lq*128]
+  bf16* k_cache;         // [B, lkv, S_max, 128]
+  bf16* v_cache;
+  int B, T, past, S_max, lq, lkv;
+  float eps, theta;
+};
+hipError_t qkv_norm_rope_store(const QkvArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const bf16* q;         // [B*T, lq*128]
+  const bf16* k_cache;   // [B, lkv, S_max, 128]
+  const bf16* v_cache;
+  bf16* out;             // [B*T, lq*128]
+  float* scratch;        // decode split partials
+  int B, T, past, S_max, lq, lkv;
+};
+size_t attn_decode_scratch_bytes(int B, int lq, int lkv, int ctx);
+hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
+hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
+
+}  // namespace tps

@@ -1,0 +1,320 @@
+// C ABI of libtpshard: argument validation, per-rank sizes, workspace
+// layout and the launch sequence of each entry point.  See tpshard.h.
+//
+// Per-rank sizes follow "8. How several ranks share one ledger" ("Weights
+// are cut by name": even chunks along dim 0 / dim 1, one whole kv head per
+// rank when there are fewer kv heads than ranks, vocab rows in ceil(V/n)
+// blocks) and "Tensor parallelism from scratch" ("KV heads and the limit on
+// TP": head counts that do not divide are rejected).
+#include <hip/hip_runtime.h>
+
+#include "../../include/tpshard.h"
+#include "common.h"
+
+using namespace tps;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cfg(const tp_cfg* c, tp_local* L) {
+  if (!c) return TP_ERR_NULL;
+  if (c->tp_size < 1 || c->tp_rank < 0 || c->tp_rank >= c->tp_size) return TP_ERR_RANK;
+  if (c->dtype != TP_F32 && c->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (c->hidden <= 0 || c->intermediate < 0 || c->n_q_heads < 0 || c->n_kv_heads < 0 || c->vocab < 0 ||
+      c->head_dim < 0)
+    return TP_ERR_SHAPE;
+  const int n = c->tp_size, r = c->tp_rank;
+  if (c->n_q_heads % n || c->intermediate % n) return TP_ERR_SHAPE;
+  tp_local o{};
+  o.lq = c->n_q_heads / n;
+  if (c->n_q_heads == 0 && c->n_kv_heads == 0) {
+    o.lkv = 0;
+    o.kv_head0 = 0;
+  } else {
+    if (c->n_q_heads == 0 || c->n_kv_heads == 0 || c->head_dim <= 0) return TP_ERR_SHAPE;
+    if (c->n_q_heads % c->n_kv_heads) return TP_ERR_SHAPE;   // GQA groups must be whole
+    if (c->n_kv_heads >= n) {
+      if (c->n_kv_heads % n) return TP_ERR_SHAPE;
+      o.lkv = c->n_kv_heads / n;
+      o.kv_head0 = r * o.lkv;
+    } else {
+      if (n % c->n_kv_heads) return TP_ERR_SHAPE;
+      o.lkv = 1;                                             // replicated kv head
+      o.kv_head0 = (int32_t)((int64_t)r * c->n_kv_heads / n);
+    }
+  }
+  o.li = c->intermediate / n;
+  o.n_qkv = (int64_t)(o.lq + 2 * o.lkv) * c->head_dim;
+  const int64_t per = (c->vocab + n - 1) / n;
+  o.vocab_start = (int64_t)r * per < c->vocab ? (int64_t)r * per : c->vocab;
+  o.vocab_end = (int64_t)(r + 1) * per < c->vocab ? (int64_t)(r + 1) * per : c->vocab;
+  if (L) *L = o;
+  return TP_OK;
+}
+
+int esize_of(const tp_cfg* c) { return c->dtype == TP_BF16 ? 2 : 4; }
+
+// workspace layout of tp_qkv_attn (each region 256-byte aligned)
+struct AttnWs {
+  size_t qkv, q, attn, scratch, scratch_bytes, total;
+};
+AttnWs attn_ws(const tp_cfg* c, const tp_local& L, int64_t B, int64_t T, int64_t past) {
+  const int64_t M = B * T;
+  AttnWs w{};
+  w.qkv = 0;
+  w.q = w.qkv + align_up((size_t)(M * L.n_qkv) * 4);
+  w.attn = w.q + align_up((size_t)(M * L.lq * 128) * 2);
+  w.scratch = w.attn + align_up((size_t)(M * L.lq * 128) * 2);
+  size_t sb = gemm_scratch_bytes(M, L.n_qkv, c->hidden, EPI_F32);
+  const size_t so = gemm_scratch_bytes(M, c->hidden, (int64_t)L.lq * 128, EPI_BF16);
+  if (so > sb) sb = so;
+  if (T == 1 && B > 0) {
+    const size_t sd = attn_decode_scratch_bytes((int)B, L.lq, L.lkv, (int)(past + 1));
+    if (sd > sb) sb = sd;
+  }
+  w.scratch_bytes = align_up(sb);
+  w.total = w.scratch + w.scratch_bytes;
+  return w;
+}
+
+struct MlpWs {
+  size_t h, scratch, scratch_bytes, total;
+};
+MlpWs mlp_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
+  MlpWs w{};
+  w.h = 0;
+  w.scratch = align_up((size_t)(M * L.li) * esize_of(c));
+  size_t sb = 0;
+  if (c->dtype == TP_BF16) {
+    sb = gemm_scratch_bytes(M, 2 * (int64_t)L.li, c->hidden, EPI_SILU_BF16);
+    const size_t sd = gemm_scratch_bytes(M, c->hidden, L.li, EPI_BF16);
+    if (sd > sb) sb = sd;
+  }
+  w.scratch_bytes = align_up(sb);
+  w.total = w.scratch + w.scratch_bytes;
+  return w;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int tp_local_dims(const tp_cfg* cfg, tp_local* out) {
+  if (!out) return TP_ERR_NULL;
+  return check_cfg(cfg, out);
+}
+
+const char* tp_status_str(int s) {
+  switch (s) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULL: return "null pointer";
+    case TP_ERR_RANK: return "tp_rank outside [0, tp_size)";
+    case TP_ERR_SHAPE: return "shape not splittable across ranks or not supported";
+    case TP_ERR_DTYPE: return "dtype not supported";
+    case TP_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case TP_ERR_WORKSPACE: return "workspace too small";
+    case TP_ERR_RANGE: return "size out of range (negative, or past_len + T > S_max)";
+    case TP_ERR_LAUNCH: return "kernel launch failed";
+    case TP_ERR_KIND: return "unknown weight kind or op";
+    default: return "unknown status";
+  }
+}
+
+int tp_workspace_bytes(const tp_cfg* cfg, int op, int64_t B, int64_t T, int64_t past_len, size_t* out_bytes) {
+  if (!out_bytes) return TP_ERR_NULL;
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (B < 0 || T < 0 || past_len < 0) return TP_ERR_RANGE;
+  if (op == TP_OP_ATTN) {
+    if (L.lq == 0) return TP_ERR_SHAPE;
+    *out_bytes = attn_ws(cfg, L, B, T, past_len).total;
+  } else if (op == TP_OP_MLP) {
+    *out_bytes = mlp_ws(cfg, L, B * T).total;
+  } else {
+    return TP_ERR_KIND;
+  }
+  return TP_OK;
+}
+
+int tp_shard_weights(const tp_cfg* cfg, int kind, const void* full, void* dst, void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (kind < TP_W_Q || kind > TP_W_VOCAB) return TP_ERR_KIND;
+  if (!full || !dst) return TP_ERR_NULL;
+  if (!aligned16(full) || !aligned16(dst)) return TP_ERR_ALIGN;
+  const int es = esize_of(cfg);
+  const int64_t H = cfg->hidden, d = cfg->head_dim, r = cfg->tp_rank;
+  const bool heads = L.lq > 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* dp = static_cast<char*>(dst);
+  hipError_t e = hipSuccess;
+  switch (kind) {
+    case TP_W_Q:
+      if (!heads) return TP_ERR_SHAPE;
+      e = copy2d(full, H, r * L.lq * d, 0, dp, H, L.lq * d, H, es, s);
+      break;
+    case TP_W_K:
+      if (!heads) return TP_ERR_SHAPE;
+      e = copy2d(full, H, (int64_t)L.kv_head0 * d, 0, dp + (L.lq * d * H) * es, H, L.lkv * d, H, es, s);
+      break;
+    case TP_W_V:
+      if (!heads) return TP_ERR_SHAPE;
+      e = copy2d(full, H, (int64_t)L.kv_head0 * d, 0, dp + ((L.lq + L.lkv) * d * H) * es, H, L.lkv * d, H, es, s);
+      break;
+    case TP_W_O:
+      if (!heads) return TP_ERR_SHAPE;
+      e = copy2d(full, (int64_t)cfg->n_q_heads * d, 0, r * L.lq * d, dp, L.lq * d, H, L.lq * d, es, s);
+      break;
+    case TP_W_GATE:
+      if (L.li == 0) return TP_ERR_SHAPE;
+      e = copy2d(full, H, r * L.li, 0, dp, H, L.li, H, es, s);
+      break;
+    case TP_W_UP:
+      if (L.li == 0) return TP_ERR_SHAPE;
+      e = copy2d(full, H, r * L.li, 0, dp + ((int64_t)L.li * H) * es, H, L.li, H, es, s);
+      break;
+    case TP_W_DOWN:
+      if (L.li == 0) return TP_ERR_SHAPE;
+      e = copy2d(full, cfg->intermediate, 0, r * L.li, dp, L.li, H, L.li, es, s);
+      break;
+    case TP_W_VOCAB:
+      if (cfg->vocab == 0) return TP_ERR_SHAPE;
+      e = copy2d(full, H, L.vocab_start, 0, dp, H, L.vocab_end - L.vocab_start, H, es, s);
+      break;
+  }
+  return launched(e);
+}
+
+int tp_embed_vocab(const tp_cfg* cfg, const int32_t* ids, int64_t n_tokens, const void* vocab_local, void* out,
+                   void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (n_tokens < 0) return TP_ERR_RANGE;
+  if (!ids || !vocab_local || !out) return TP_ERR_NULL;
+  if (!aligned16(ids) || !aligned16(vocab_local) || !aligned16(out)) return TP_ERR_ALIGN;
+  if (((int64_t)cfg->hidden * esize_of(cfg)) % 16) return TP_ERR_SHAPE;
+  if (n_tokens == 0) return TP_OK;
+  return launched(embed_masked(ids, n_tokens, vocab_local, L.vocab_start, L.vocab_end, cfg->hidden,
+                               esize_of(cfg), out, static_cast<hipStream_t>(stream)));
+}
+
+int tp_qkv_attn(const tp_cfg* cfg, const void* x, int32_t B, int32_t T, int32_t past_len, const void* w_qkv,
+                const void* q_norm_w, const void* k_norm_w, const void* w_o, void* k_cache, void* v_cache,
+                int32_t S_max, void* q_out_opt, void* attn_out_opt, void* out_partial, void* workspace,
+                size_t ws_bytes, void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (L.lq == 0 || cfg->head_dim != 128 || cfg->hidden % 8) return TP_ERR_SHAPE;
+  const int rep = L.lq / L.lkv;
+  if (L.lq % L.lkv || (rep != 1 && rep != 2 && rep != 4 && rep != 8 && rep != 16)) return TP_ERR_SHAPE;
+  if (B < 0 || T < 0 || past_len < 0 || S_max < 0) return TP_ERR_RANGE;
+  if ((int64_t)past_len + T > S_max) return TP_ERR_RANGE;
+  if (!x || !w_qkv || !q_norm_w || !k_norm_w || !w_o || !k_cache || !v_cache || !out_partial)
+    return TP_ERR_NULL;
+  const void* ptrs[] = {x, w_qkv, q_norm_w, k_norm_w, w_o, k_cache, v_cache, out_partial};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TP_ERR_ALIGN;
+  if ((q_out_opt && !aligned16(q_out_opt)) || (attn_out_opt && !aligned16(attn_out_opt))) return TP_ERR_ALIGN;
+  if ((int64_t)B * T == 0) return TP_OK;
+  const AttnWs w = attn_ws(cfg, L, B, T, past_len);
+  if (!workspace) return TP_ERR_NULL;
+  if (!aligned16(workspace)) return TP_ERR_ALIGN;
+  if (ws_bytes < w.total) return TP_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t M = (int64_t)B * T, H = cfg->hidden, lqd = (int64_t)L.lq * 128;
+  float* qkv = reinterpret_cast<float*>(ws + w.qkv);
+  bf16* q = q_out_opt ? static_cast<bf16*>(q_out_opt) : reinterpret_cast<bf16*>(ws + w.q);
+  bf16* attn = attn_out_opt ? static_cast<bf16*>(attn_out_opt) : reinterpret_cast<bf16*>(ws + w.attn);
+  void* scratch = ws + w.scratch;
+
+  // 1. merged column-parallel projection (fp32 result)
+  GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(w_qkv), qkv, M, L.n_qkv, H, H, H, L.n_qkv, 0};
+  hipError_t e = gemm_bf16(g, EPI_F32, scratch, w.scratch_bytes, s);
+  if (e != hipSuccess) return TP_ERR_LAUNCH;
+  // 2. QK-norm, RoPE, cache append
+  QkvArgs qa{qkv, static_cast<const bf16*>(q_norm_w), static_cast<const bf16*>(k_norm_w), q,
+             static_cast<bf16*>(k_cache), static_cast<bf16*>(v_cache), B, T, past_len, S_max, L.lq, L.lkv,
+             cfg->rms_eps, cfg->rope_theta};
+  e = qkv_norm_rope_store(qa, s);
+  if (e != hipSuccess) return TP_ERR_LAUNCH;
+  // 3. attention over the local heads
+  AttnArgs aa{q, static_cast<const bf16*>(k_cache), static_cast<const bf16*>(v_cache), attn,
+              reinterpret_cast<float*>(scratch), B, T, past_len, S_max, L.lq, L.lkv};
+  e = T == 1 ? attn_decode(aa, s) : attn_prefill(aa, s);
+  if (e != hipSuccess) return TP_ERR_LAUNCH;
+  // 4. row-parallel o_proj -> partial sum
+  GemmProblem go{attn, static_cast<const bf16*>(w_o), out_partial, M, H, lqd, lqd, lqd, H, 0};
+  return launched(gemm_bf16(go, EPI_BF16, scratch, w.scratch_bytes, s));
+}
+
+int tp_mlp(const tp_cfg* cfg, const void* x, int64_t M, const void* w_gate_up, const void* w_down, void* h_opt,
+           void* out_partial, void* workspace, size_t ws_bytes, void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (L.li == 0 || cfg->hidden % 8 || L.li % 8) return TP_ERR_SHAPE;
+  if (M < 0) return TP_ERR_RANGE;
+  if (!x || !w_gate_up || !w_down || !out_partial) return TP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out_partial) ||
+      (h_opt && !aligned16(h_opt)))
+    return TP_ERR_ALIGN;
+  if (M == 0) return TP_OK;
+  const MlpWs w = mlp_ws(cfg, L, M);
+  if (!h_opt || w.scratch_bytes) {
+    if (!workspace) return TP_ERR_NULL;
+    if (!aligned16(workspace)) return TP_ERR_ALIGN;
+    if (ws_bytes < w.total) return TP_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t H = cfg->hidden, li = L.li;
+  void* h = h_opt ? h_opt : ws + w.h;
+  if (cfg->dtype == TP_F32) {
+    hipError_t e = gemm_f32(static_cast<const float*>(x), static_cast<const float*>(w_gate_up),
+                            static_cast<float*>(h), M, 2 * li, H, (int)li, s);
+    if (e != hipSuccess) return TP_ERR_LAUNCH;
+    return launched(gemm_f32(static_cast<const float*>(h), static_cast<const float*>(w_down),
+                             static_cast<float*>(out_partial), M, H, li, 0, s));
+  }
+  void* scratch = ws ? ws + w.scratch : nullptr;
+  // gate_up column-parallel GEMM with silu(gate) * up fused
+  GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(w_gate_up), h, M, 2 * li, H, H, H, li, li};
+  hipError_t e = gemm_bf16(g, EPI_SILU_BF16, scratch, w.scratch_bytes, s);
+  if (e != hipSuccess) return TP_ERR_LAUNCH;
+  // down row-parallel GEMM -> partial sum
+  GemmProblem gd{static_cast<const bf16*>(h), static_cast<const bf16*>(w_down), out_partial, M, H, li, li, li, H, 0};
+  return launched(gemm_bf16(gd, EPI_BF16, scratch, w.scratch_bytes, s));
+}
+
+int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local, void* logits_local,
+               void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (cfg->vocab == 0 || cfg->hidden % 8) return TP_ERR_SHAPE;
+  if (M < 0) return TP_ERR_RANGE;
+  if (!x || !vocab_local || !logits_local) return TP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(vocab_local) || !aligned16(logits_local)) return TP_ERR_ALIGN;
+  const int64_t N = L.vocab_end - L.vocab_start, H = cfg->hidden;
+  if (M == 0 || N == 0) return TP_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg->dtype == TP_F32)
+    return launched(gemm_f32(static_cast<const float*>(x), static_cast<const float*>(vocab_local),
+                             static_cast<float*>(logits_local), M, N, H, 0, s));
+  GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), logits_local, M, N, H, H, H, N, 0};
+  return launched(gemm_bf16(g, EPI_BF16, nullptr, 0, s));
+}
+
+}  // extern "C"

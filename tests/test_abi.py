@@ -1,0 +1,172 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and validates arguments before any launch.  No GPU work:
+every device entry point here is called with arguments that validation
+rejects (or with an empty size), so nothing is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+import tensor_transformer_layer_rank_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+OK, E_NULL, E_RANK, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_RANGE, E_LAUNCH, E_KIND = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(tp_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(tp.EXPORTS)
+    L = tp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(tp.tp_cfg) == 48
+    assert ctypes.sizeof(tp.tp_local) == 40
+
+
+def _ocfg(c: tp.Cfg):
+    return O.Cfg(hidden=c.hidden, intermediate=c.intermediate, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
+                 head_dim=c.head_dim, vocab=c.vocab, tp_size=c.tp_size, tp_rank=c.tp_rank)
+
+
+SHAPES = [
+    dict(hidden=1024, intermediate=3072, n_q_heads=16, n_kv_heads=8, vocab=151936),    # Qwen3-0.6B
+    dict(hidden=5120, intermediate=25600, n_q_heads=64, n_kv_heads=8, vocab=151936),   # Qwen3-32B
+    dict(hidden=64, intermediate=192, n_q_heads=4, n_kv_heads=1, vocab=37),
+    dict(hidden=64, intermediate=192, n_q_heads=12, n_kv_heads=3, vocab=10),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 6, 8, 16])
+def test_local_dims_match_oracle(shape, n):
+    for r in range(n):
+        c = tp.Cfg(**shape, tp_size=n, tp_rank=r)
+        try:
+            ref = O.local_dims(_ocfg(c))
+        except ValueError:
+            with pytest.raises(tp.TpError) as ei:
+                tp.tp_local_dims(c)
+            assert ei.value.status == E_SHAPE
+            continue
+        got = tp.tp_local_dims(c)
+        assert (got.lq, got.lkv, got.kv_head0, got.li, got.n_qkv, got.vocab_start, got.vocab_end) == \
+               (ref.lq, ref.lkv, ref.kv_head0, ref.li, ref.n_qkv, ref.vocab_start, ref.vocab_end)
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except tp.TpError as e:
+        return e.status
+    return OK
+
+
+def test_config_errors():
+    base = dict(hidden=64, intermediate=192, n_q_heads=4, n_kv_heads=2, vocab=100)
+    assert _status(tp.tp_local_dims, tp.Cfg(**base, tp_size=2, tp_rank=2)) == E_RANK
+    assert _status(tp.tp_local_dims, tp.Cfg(**base, tp_size=0, tp_rank=0)) == E_RANK
+    assert _status(tp.tp_local_dims, tp.Cfg(**base, tp_size=2, tp_rank=-1)) == E_RANK
+    assert _status(tp.tp_local_dims, tp.Cfg(**{**base, "n_q_heads": 6}, tp_size=4)) == E_SHAPE
+    assert _status(tp.tp_local_dims, tp.Cfg(**{**base, "intermediate": 190}, tp_size=4)) == E_SHAPE
+    assert _status(tp.tp_local_dims, tp.Cfg(**{**base, "n_q_heads": 12, "n_kv_heads": 4}, tp_size=6)) == E_SHAPE
+    assert _status(tp.tp_local_dims, tp.Cfg(**base, tp_size=2, dtype=7)) == E_DTYPE
+    assert _status(tp.tp_local_dims, tp.Cfg(**{**base, "hidden": 0}, tp_size=2)) == E_SHAPE
+    assert tp.tp_status_str(E_WS) == "workspace too small"
+
+
+class Fake:
+    """A stand-in 'tensor' with a fake device address; used only where the
+    library must reject the call before launching anything."""
+
+    def __init__(self, addr, numel=0, esize=1):
+        self.addr, self.n, self.es = addr, numel, esize
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return self.es
+
+
+class NullStream:
+    cuda_stream = 0
+
+
+A = Fake(1 << 40)           # 16-byte aligned
+MIS = Fake((1 << 40) + 8)   # misaligned
+
+
+def test_shard_and_embed_validation():
+    c = tp.Cfg(hidden=64, intermediate=192, n_q_heads=4, n_kv_heads=2, vocab=100, tp_size=2)
+    s = NullStream()
+    assert _status(tp.tp_shard_weights, c, 99, A, A, s) == E_KIND
+    assert _status(tp.tp_shard_weights, c, tp.TP_W_Q, None, A, s) == E_NULL
+    assert _status(tp.tp_shard_weights, c, tp.TP_W_Q, A, MIS, s) == E_ALIGN
+    cm = tp.Cfg(hidden=64, intermediate=192, tp_size=2)          # MLP-only shape
+    assert _status(tp.tp_shard_weights, cm, tp.TP_W_K, A, A, s) == E_SHAPE
+    assert _status(tp.tp_shard_weights, cm, tp.TP_W_VOCAB, A, A, s) == E_SHAPE
+    ids = Fake(1 << 40, numel=0)
+    assert _status(tp.tp_embed_vocab, c, ids, A, A, s) == OK           # empty: no-op
+    assert _status(tp.tp_embed_vocab, c, Fake((1 << 40) + 4, 5), A, A, s) == E_ALIGN
+    assert _status(tp.tp_embed_vocab, c, Fake(1 << 40, 5), None, A, s) == E_NULL
+
+
+def test_attn_validation():
+    c = tp.Cfg(hidden=256, intermediate=512, n_q_heads=4, n_kv_heads=2, head_dim=128, tp_size=2)
+    s = NullStream()
+    args = lambda **kw: dict(dict(cfg=c, x=A, B=2, T=3, past_len=4, w_qkv=A, q_norm_w=A, k_norm_w=A, w_o=A,
+                                  k_cache=A, v_cache=A, S_max=16, out_partial=A, workspace=Fake(1 << 40, 16, 1),
+                                  stream=s), **kw)
+
+    def st(**kw):
+        try:
+            tp.tp_qkv_attn(**args(**kw))
+        except tp.TpError as e:
+            return e.status
+        return OK
+
+    assert st(workspace=Fake(1 << 40, 16, 1)) == E_WS
+    assert st(past_len=14) == E_RANGE                     # 14 + 3 > 16
+    assert st(T=-1) == E_RANGE
+    assert st(x=None) == E_NULL
+    assert st(k_cache=MIS) == E_ALIGN
+    assert st(attn_out=MIS) == E_ALIGN
+    assert st(workspace=None) == E_NULL
+    assert st(B=0) == OK                                  # empty: no-op
+    assert st(cfg=tp.Cfg(**{**c.__dict__, "dtype": tp.TP_F32})) == E_DTYPE
+    assert st(cfg=tp.Cfg(**{**c.__dict__, "head_dim": 64})) == E_SHAPE
+    assert st(cfg=tp.Cfg(**{**c.__dict__, "hidden": 260})) == E_SHAPE
+    need = tp.tp_workspace_bytes(c, tp.TP_OP_ATTN, 2, 3, 4)
+    assert need >= (2 * 3) * (2 + 2 * 1) * 128 * 4     # at least the fp32 qkv projection
+
+
+def test_mlp_and_lm_head_validation():
+    c = tp.Cfg(hidden=256, intermediate=512, tp_size=2)
+    s = NullStream()
+    assert _status(tp.tp_mlp, c, A, 0, A, A, A, None, None, s) == OK        # M = 0
+    assert _status(tp.tp_mlp, c, A, -1, A, A, A, None, None, s) == E_RANGE
+    assert _status(tp.tp_mlp, c, A, 4, A, A, A, None, None, s) == E_NULL     # no workspace
+    assert _status(tp.tp_mlp, c, A, 4, A, A, A, Fake(1 << 40, 8, 1), None, s) == E_WS
+    assert _status(tp.tp_mlp, tp.Cfg(hidden=256, intermediate=20, tp_size=2), A, 4, A, A, A,
+                   Fake(1 << 40, 1 << 20, 1), None, s) == E_SHAPE              # li = 10
+    assert tp.tp_workspace_bytes(c, tp.TP_OP_MLP, 4, 1) >= 4 * 256 * 2
+    cv = tp.Cfg(hidden=256, vocab=1000, tp_size=4, tp_rank=3)
+    assert _status(tp.tp_lm_head, cv, A, 0, A, A, s) == OK
+    assert _status(tp.tp_lm_head, cv, A, 4, MIS, A, s) == E_ALIGN
+    assert _status(tp.tp_lm_head, tp.Cfg(hidden=256, tp_size=1), A, 4, A, A, s) == E_SHAPE

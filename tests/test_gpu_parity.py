@@ -1,0 +1,454 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: shard maps and the masked embedding bit-exact; numerics
+max|gpu - oracle| / max|oracle| <= 1e-2 per tensor for bf16 (fp32 accumulate)
+and <= 1e-5 for the fp32 workload.  Mid-size cases (several tiles plus ragged
+tails in M, N and K) are compared element by element; the five full-size
+workloads are compared on sampled rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import tensor_transformer_layer_rank_amd as tp
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-5
+
+
+def relerr(gpu, ref):
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    den = np.max(np.abs(ref)) if ref.size else 1.0
+    return float(np.max(np.abs(gpu - ref)) / max(den, 1e-30)) if ref.size else 0.0
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bits16(t):
+    return t.detach().cpu().view(torch.int16).numpy()
+
+
+def tcfg(w, r, n=None, dtype=tp.TP_BF16):
+    return tp.Cfg(hidden=w["hidden"], intermediate=w["intermediate"], n_q_heads=w["n_q_heads"],
+                  n_kv_heads=w["n_kv_heads"], head_dim=w["head_dim"], tp_size=n or w["tp"], tp_rank=r,
+                  dtype=dtype, vocab=w.get("vocab", 0))
+
+
+def ocfg(w, r, n=None):
+    return O.Cfg(hidden=w["hidden"], intermediate=w["intermediate"], n_q_heads=w["n_q_heads"],
+                 n_kv_heads=w["n_kv_heads"], head_dim=w["head_dim"], vocab=w.get("vocab", 0),
+                 tp_size=n or w["tp"], tp_rank=r)
+
+
+# mid-size shapes: several tiles and ragged tails; each exercises one GQA shape
+MID = {
+    "rep2": dict(hidden=520, intermediate=1568, n_q_heads=8, n_kv_heads=4, head_dim=128, vocab=1000, tp=2),
+    "rep4-replicated": dict(hidden=256, intermediate=512, n_q_heads=8, n_kv_heads=2, head_dim=128, vocab=300, tp=4),
+    "rep8": dict(hidden=512, intermediate=1024, n_q_heads=16, n_kv_heads=2, head_dim=128, vocab=777, tp=2),
+    "rep1": dict(hidden=264, intermediate=528, n_q_heads=4, n_kv_heads=4, head_dim=128, vocab=64, tp=2),
+    "rep16": dict(hidden=384, intermediate=768, n_q_heads=32, n_kv_heads=2, head_dim=128, vocab=100, tp=2),
+}
+MID_WID = {k: 100 + i for i, k in enumerate(MID)}
+
+
+class Rank:
+    """One rank's local weights, sharded on the device by tp_shard_weights
+    from the full weights."""
+
+    def __init__(self, w, r, W, n=None):
+        self.c = tcfg(w, r, n)
+        self.L = tp.tp_local_dims(self.c)
+        L, H = self.L, w["hidden"]
+        dt = torch.bfloat16
+        self.qkv = torch.empty(L.n_qkv, H, dtype=dt, device=DEV)
+        self.gu = torch.empty(2 * L.li, H, dtype=dt, device=DEV)
+        self.o = torch.empty(H, L.lq * 128, dtype=dt, device=DEV)
+        self.down = torch.empty(H, L.li, dtype=dt, device=DEV)
+        for kind, name, dst in ((tp.TP_W_Q, "q", self.qkv), (tp.TP_W_K, "k", self.qkv), (tp.TP_W_V, "v", self.qkv),
+                                (tp.TP_W_GATE, "gate", self.gu), (tp.TP_W_UP, "up", self.gu),
+                                (tp.TP_W_O, "o", self.o), (tp.TP_W_DOWN, "down", self.down)):
+            tp.tp_shard_weights(self.c, kind, W[name], dst)
+        self.qn, self.kn = W["q_norm"], W["k_norm"]
+
+
+def gpu_weights(w, wid):
+    return {k: v.to(DEV) for k, v in synth.full_weights(wid, w).items()}
+
+
+def shard64(oc, kind, Wt):
+    """Oracle shard of a full bf16 weight, taken on its bit patterns, then
+    widened to float64 (cheaper than widening the full matrix)."""
+    b = O.shard(oc, kind, Wt.view(torch.int16).numpy())
+    return synth.to_f64(torch.from_numpy(np.ascontiguousarray(b)).view(torch.bfloat16))
+
+
+def oracle_rank_weights(oc, Wc):
+    """The oracle's own shard + merge of the CPU copies of the full weights."""
+    qkv = O.merge_qkv(O.shard(oc, O.W_Q, Wc["q"]), O.shard(oc, O.W_K, Wc["k"]), O.shard(oc, O.W_V, Wc["v"]))
+    gu = O.merge_gate_up(O.shard(oc, O.W_GATE, Wc["gate"]), O.shard(oc, O.W_UP, Wc["up"]))
+    return qkv, gu, O.shard(oc, O.W_O, Wc["o"]), O.shard(oc, O.W_DOWN, Wc["down"])
+
+
+def run_attn(rk, x, B, T, past, kc, vc, S_max):
+    L = rk.L
+    M = B * T
+    H = x.shape[1]
+    ws = torch.empty(tp.tp_workspace_bytes(rk.c, tp.TP_OP_ATTN, B, T, past), dtype=torch.uint8, device=DEV)
+    q = torch.empty(M, L.lq * 128, dtype=torch.bfloat16, device=DEV)
+    a = torch.empty_like(q)
+    part = torch.empty(M, H, dtype=torch.bfloat16, device=DEV)
+    tp.tp_qkv_attn(rk.c, x, B, T, past, rk.qkv, rk.qn, rk.kn, rk.o, kc, vc, S_max, part, ws, q_out=q, attn_out=a)
+    return q, a, part
+
+
+def run_mlp(rk, x, M):
+    ws = torch.empty(tp.tp_workspace_bytes(rk.c, tp.TP_OP_MLP, M, 1), dtype=torch.uint8, device=DEV)
+    h = torch.empty(M, rk.L.li, dtype=x.dtype, device=DEV)
+    part = torch.empty(M, x.shape[1], dtype=x.dtype, device=DEV)
+    tp.tp_mlp(rk.c, x, M, rk.gu, rk.down, part, ws, h_out=h)
+    return h, part
+
+
+# ------------------------------------------------------------------ shards and embedding
+
+@pytest.mark.parametrize("name", list(MID) + ["w2", "w5"])
+def test_shard_weights_bit_exact(name):
+    if name in MID:
+        w, wid = MID[name], MID_WID[name]
+    else:
+        wid = int(name[1])
+        w = synth.WORKLOADS[wid]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    Wb = {k: v.view(torch.int16).numpy() for k, v in W.items()}
+    n = w["tp"]
+    ranks = range(n) if n <= 4 else [0, 1, 2, n - 1]
+    for r in ranks:
+        rk = Rank(w, r, Wg)
+        qkv, gu, o, down = oracle_rank_weights(ocfg(w, r), Wb)
+        assert np.array_equal(bits16(rk.qkv), qkv), (name, r, "qkv")
+        assert np.array_equal(bits16(rk.gu), gu), (name, r, "gate_up")
+        assert np.array_equal(bits16(rk.o), o), (name, r, "o")
+        assert np.array_equal(bits16(rk.down), down), (name, r, "down")
+
+
+def test_shard_weights_fp32_and_vocab():
+    w = synth.WORKLOADS[1]
+    W = synth.mlp_weights(1, w, torch.float32)
+    for r in range(2):
+        c = tcfg(w, r, dtype=tp.TP_F32)
+        L = tp.tp_local_dims(c)
+        gu = torch.empty(2 * L.li, w["hidden"], device=DEV)
+        down = torch.empty(w["hidden"], L.li, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_GATE, W["gate"].to(DEV), gu)
+        tp.tp_shard_weights(c, tp.TP_W_UP, W["up"].to(DEV), gu)
+        tp.tp_shard_weights(c, tp.TP_W_DOWN, W["down"].to(DEV), down)
+        oc = ocfg(w, r)
+        ref = O.merge_gate_up(O.shard(oc, O.W_GATE, W["gate"].numpy()), O.shard(oc, O.W_UP, W["up"].numpy()))
+        assert np.array_equal(gu.cpu().numpy().view(np.int32), ref.view(np.int32))
+        assert np.array_equal(down.cpu().numpy().view(np.int32), O.shard(oc, O.W_DOWN, W["down"].numpy()).view(np.int32))
+    # vocab rows, uneven last shard (V = 1000 over 3 ranks: 334, 334, 332)
+    V, H = 1000, 136
+    E = synth.embedding(7, V, H)
+    for r in range(3):
+        c = tp.Cfg(hidden=H, vocab=V, tp_size=3, tp_rank=r)
+        L = tp.tp_local_dims(c)
+        dst = torch.empty(L.vocab_end - L.vocab_start, H, dtype=torch.bfloat16, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_VOCAB, E.to(DEV), dst)
+        ref = O.shard(O.Cfg(hidden=H, vocab=V, tp_size=3, tp_rank=r), O.W_VOCAB, E.view(torch.int16).numpy())
+        assert np.array_equal(bits16(dst), ref)
+
+
+@pytest.mark.parametrize("case", ["w3", "ragged"])
+def test_embed_vocab_bit_exact_and_vocab_sum(case):
+    if case == "w3":
+        w = synth.WORKLOADS[3]
+        V, H, n, n_ids = w["vocab"], w["hidden"], w["tp"], w["n_ids"]
+        E = synth.embedding(3, V, H)
+        ids = synth.token_ids(3, n_ids, V)
+    else:
+        V, H, n = 1001, 72, 3
+        E = synth.embedding(9, V, H)
+        ids = synth.token_ids(9, 37, V)
+    # out-of-vocab and negative ids give zero rows on every rank
+    ids = torch.cat([ids, torch.tensor([0, V - 1, V, V + 17, -1, -V], dtype=torch.int32)])
+    Eg, idg = E.to(DEV), ids.to(DEV)
+    Eb = E.view(torch.int16).numpy()
+    total = torch.zeros(ids.numel(), H, dtype=torch.float32, device=DEV)
+    for r in range(n):
+        c = tp.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        L = tp.tp_local_dims(c)
+        shard = torch.empty(L.vocab_end - L.vocab_start, H, dtype=torch.bfloat16, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_VOCAB, Eg, shard)
+        out = torch.full((ids.numel(), H), 7.0, dtype=torch.bfloat16, device=DEV)
+        tp.tp_embed_vocab(c, idg, shard, out)
+        oc = O.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        ref = O.embed_vocab(ids.numpy(), O.shard(oc, O.W_VOCAB, Eb), L.vocab_start, L.vocab_end)
+        assert np.array_equal(bits16(out), ref), r
+        total += out.float()
+    valid = (ids >= 0) & (ids < V)
+    assert torch.equal(total.cpu()[valid], E[ids[valid].long()].float())
+    assert torch.count_nonzero(total.cpu()[~valid]) == 0
+
+
+# ------------------------------------------------------------------ lm_head
+
+@pytest.mark.parametrize("case", ["w3", "mid"])
+def test_lm_head(case):
+    if case == "w3":
+        w = synth.WORKLOADS[3]
+        V, H, n, M = w["vocab"], w["hidden"], w["tp"], w["n_ids"]
+        E = synth.embedding(3, V, H)
+        x = synth.activations(3, M, H)
+        rows = np.unique(np.concatenate([[0, 1, M - 1], np.random.default_rng(3).integers(0, M, 13)]))
+        ranks = [0, 1]
+    else:
+        V, H, n, M = 777, 520, 2, 300
+        E = synth.embedding(11, V, H)
+        x = synth.activations(11, M, H)
+        rows = np.arange(M)
+        ranks = [0, 1]
+    Eg, xg = E.to(DEV), x.to(DEV)
+    for r in ranks:
+        c = tp.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        L = tp.tp_local_dims(c)
+        shard = torch.empty(L.vocab_end - L.vocab_start, H, dtype=torch.bfloat16, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_VOCAB, Eg, shard)
+        logits = torch.empty(M, L.vocab_end - L.vocab_start, dtype=torch.bfloat16, device=DEV)
+        tp.tp_lm_head(c, xg, M, shard, logits)
+        torch.cuda.synchronize()
+        ref = O.lm_head(synth.to_f64(x)[rows], synth.to_f64(E)[L.vocab_start:L.vocab_end])
+        err = relerr(f64(logits)[rows], ref)
+        assert err <= TOL_BF16, (case, r, err)
+
+
+# ------------------------------------------------------------------ MLP
+
+def test_mlp_fp32_tiny_both_ranks_and_row_sum():
+    w = synth.WORKLOADS[1]
+    W = synth.mlp_weights(1, w, torch.float32)
+    x = synth.activations(1, w["mlp_tokens"], w["hidden"], torch.float32)
+    xc = synth.to_f64(x)
+    Wc = {k: synth.to_f64(v) for k, v in W.items()}
+    psum = torch.zeros(x.shape, dtype=torch.float64)
+    for r in range(w["tp"]):
+        c = tcfg(w, r, dtype=tp.TP_F32)
+        L = tp.tp_local_dims(c)
+        gu = torch.empty(2 * L.li, w["hidden"], device=DEV)
+        down = torch.empty(w["hidden"], L.li, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_GATE, W["gate"].to(DEV), gu)
+        tp.tp_shard_weights(c, tp.TP_W_UP, W["up"].to(DEV), gu)
+        tp.tp_shard_weights(c, tp.TP_W_DOWN, W["down"].to(DEV), down)
+        ws = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_MLP, x.shape[0], 1) + 1, dtype=torch.uint8, device=DEV)
+        h = torch.empty(x.shape[0], L.li, device=DEV)
+        part = torch.empty(x.shape, device=DEV)
+        tp.tp_mlp(c, x.to(DEV), x.shape[0], gu, down, part, ws, h_out=h)
+        oc = ocfg(w, r)
+        gu_o = O.merge_gate_up(O.shard(oc, O.W_GATE, Wc["gate"]), O.shard(oc, O.W_UP, Wc["up"]))
+        h_ref, p_ref = O.mlp(oc, xc, gu_o, O.shard(oc, O.W_DOWN, Wc["down"]), store=O.f32)
+        assert relerr(f64(h), h_ref) <= TOL_F32
+        assert relerr(f64(part), p_ref) <= TOL_F32
+        psum += part.double().cpu()
+    # summed row-parallel partials == the unsharded MLP
+    oc1 = O.unsharded(ocfg(w, 0))
+    _, full = O.mlp(oc1, xc, O.merge_gate_up(Wc["gate"], Wc["up"]), Wc["down"], store=O.f32)
+    assert relerr(psum.numpy(), full) <= TOL_F32
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_mlp_mid_all_ranks(name):
+    w, wid = MID[name], MID_WID[name]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    Wc = {k: synth.to_f64(v) for k, v in W.items()}
+    for M in (300, 7):
+        x = synth.activations(wid, M, w["hidden"], tid=synth.T_X + 20 * M)
+        xc = synth.to_f64(x)
+        psum = torch.zeros(M, w["hidden"], dtype=torch.float64)
+        for r in range(w["tp"]):
+            rk = Rank(w, r, Wg)
+            h, part = run_mlp(rk, x.to(DEV), M)
+            oc = ocfg(w, r)
+            _, gu, _, down = oracle_rank_weights(oc, Wc)
+            h_ref, p_ref = O.mlp(oc, xc, gu, down)
+            assert relerr(f64(h), h_ref) <= TOL_BF16, (name, M, r, "h")
+            assert relerr(f64(part), p_ref) <= TOL_BF16, (name, M, r, "partial")
+            psum += part.double().cpu()
+        _, full = O.mlp(O.unsharded(ocfg(w, 0)), xc, O.merge_gate_up(Wc["gate"], Wc["up"]), Wc["down"],
+                        store=lambda v: np.asarray(v, np.float64))
+        assert relerr(psum.numpy(), full) <= TOL_BF16, (name, M, "row-sum")
+
+
+@pytest.mark.parametrize("wid", [2, 4, 5])
+def test_mlp_full_size_sampled(wid):
+    w = synth.WORKLOADS[wid]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    rk = Rank(w, 0, Wg)
+    oc = ocfg(w, 0)
+    gu = O.merge_gate_up(shard64(oc, O.W_GATE, W["gate"]), shard64(oc, O.W_UP, W["up"]))
+    down = shard64(oc, O.W_DOWN, W["down"])
+    for M in (w["prefill_T"], w["decode_B"]):
+        x = synth.activations(wid, M, w["hidden"])
+        h, part = run_mlp(rk, x.to(DEV), M)
+        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).integers(0, M, 10)]))
+        h_ref, p_ref = O.mlp(oc, synth.to_f64(x)[rows], gu, down)
+        assert relerr(f64(h)[rows], h_ref) <= TOL_BF16, (wid, M, "h")
+        assert relerr(f64(part)[rows], p_ref) <= TOL_BF16, (wid, M, "partial")
+
+
+# ------------------------------------------------------------------ attention
+
+def make_cache(w, wid, rk, B, S_max, past, n_global_kv):
+    """Rank-local caches [B, lkv, S_max, d] holding the synthetic prior
+    entries (drawn per global kv head) at positions < past; the rest is NaN
+    so that a read outside the written range shows up."""
+    L = rk.L
+    kc = torch.full((B, L.lkv, S_max, 128), float("nan"), dtype=torch.bfloat16)
+    vc = kc.clone()
+    pk = pv = None
+    if past > 0:
+        pk = synth.prior_cache(wid, synth.T_KC, B, n_global_kv, past, 128)
+        pv = synth.prior_cache(wid, synth.T_VC, B, n_global_kv, past, 128)
+        kc[:, :, :past] = pk[:, L.kv_head0:L.kv_head0 + L.lkv]
+        vc[:, :, :past] = pv[:, L.kv_head0:L.kv_head0 + L.lkv]
+    return kc.to(DEV), vc.to(DEV), pk, pv
+
+
+def check_attn(w, wid, r, B, T, past, S_max, rows=None, Wg=None, W=None, tol=TOL_BF16):
+    """Runs tp_qkv_attn for rank r and compares q, the new cache entries, the
+    attention output and the partial with the oracle (on `rows`, or all)."""
+    W = W if W is not None else synth.full_weights(wid, w)
+    Wg = Wg if Wg is not None else {k: v.to(DEV) for k, v in W.items()}
+    rk = Rank(w, r, Wg)
+    L, H, d = rk.L, w["hidden"], 128
+    M = B * T
+    x = synth.activations(wid, M, H, tid=synth.T_X + 7 * T + B)
+    kc, vc, pk, pv = make_cache(w, wid, rk, B, S_max, past, w["n_kv_heads"])
+    q, a, part = run_attn(rk, x.to(DEV), B, T, past, kc, vc, S_max)
+    torch.cuda.synchronize()
+
+    oc = ocfg(w, r)
+    qkv_o = O.merge_qkv(shard64(oc, O.W_Q, W["q"]), shard64(oc, O.W_K, W["k"]), shard64(oc, O.W_V, W["v"]))
+    wo = shard64(oc, O.W_O, W["o"])
+    qn, kn = synth.to_f64(W["q_norm"]), synth.to_f64(W["k_norm"])
+    xc = synth.to_f64(x)
+    pos = np.tile(np.arange(past, past + T), B)
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    # k, v of every new token (oracle), q of the checked rows
+    k_new, v_new = O.kv_heads(oc, xc, qkv_o, kn, pos)
+    q_ref = O.q_heads(oc, xc[rows], qkv_o, qn, pos[rows])
+    rep = L.lq // L.lkv
+    kc_g, vc_g = f64(kc), f64(vc)
+    errs = {}
+    errs["q"] = relerr(f64(q)[rows], q_ref.reshape(len(rows), -1))
+    errs["k_cache"] = relerr(kc_g[:, :, past:past + T].transpose(0, 2, 1, 3).reshape(M, L.lkv, d), k_new)
+    errs["v_cache"] = relerr(vc_g[:, :, past:past + T].transpose(0, 2, 1, 3).reshape(M, L.lkv, d), v_new)
+    if past > 0:   # prior entries untouched
+        assert np.array_equal(bits16(kc.cpu()[:, :, :past]), bits16(pk[:, L.kv_head0:L.kv_head0 + L.lkv]))
+    assert torch.isnan(kc[:, :, past + T:].float()).all() if past + T < S_max else True
+    attn_ref = np.zeros((len(rows), L.lq, d))
+    for b in range(B):
+        sel = np.nonzero(rows // T == b)[0]
+        if len(sel) == 0:
+            continue
+        kseq = np.zeros((L.lkv, past + T, d))
+        vseq = np.zeros_like(kseq)
+        if past > 0:
+            kseq[:, :past] = synth.to_f64(pk[b, L.kv_head0:L.kv_head0 + L.lkv])
+            vseq[:, :past] = synth.to_f64(pv[b, L.kv_head0:L.kv_head0 + L.lkv])
+        kseq[:, past:] = k_new[b * T:(b + 1) * T].transpose(1, 0, 2)
+        vseq[:, past:] = v_new[b * T:(b + 1) * T].transpose(1, 0, 2)
+        attn_ref[sel] = O.attend(q_ref[sel], pos[rows[sel]], kseq, vseq, rep)
+    attn_ref = O.bf16(attn_ref.reshape(len(rows), -1))
+    errs["attn"] = relerr(f64(a)[rows], attn_ref)
+    errs["partial"] = relerr(f64(part)[rows], O.bf16(attn_ref @ wo.T))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (w, r, B, T, past, errs)
+    return rk, kc, vc, part
+
+
+@pytest.mark.parametrize("name", list(MID))
+@pytest.mark.parametrize("phase", ["prefill", "prefill-after-past", "decode", "decode-ctx1"])
+def test_qkv_attn_mid(name, phase):
+    w, wid = MID[name], MID_WID[name]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    B, T, past, S_max = {"prefill": (2, 300, 0, 320), "prefill-after-past": (2, 77, 150, 240),
+                         "decode": (5, 1, 299, 310), "decode-ctx1": (3, 1, 0, 4)}[phase]
+    for r in range(w["tp"]):
+        check_attn(w, wid, r, B, T, past, S_max, Wg=Wg, W=W)
+
+
+def test_qkv_attn_row_sum_and_head_concat():
+    """Summed o_proj partials over all ranks match the unsharded oracle, and
+    concatenated per-rank attention outputs match the unsharded attention."""
+    w, wid = MID["rep4-replicated"], MID_WID["rep4-replicated"]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    B, T, past, S_max = 2, 40, 0, 48
+    x = synth.activations(wid, B * T, w["hidden"], tid=synth.T_X + 7 * T + B)
+    psum = torch.zeros(B * T, w["hidden"], dtype=torch.float64)
+    attn = []
+    for r in range(w["tp"]):
+        rk = Rank(w, r, Wg)
+        kc, vc, _, _ = make_cache(w, wid, rk, B, S_max, past, w["n_kv_heads"])
+        _, a, part = run_attn(rk, x.to(DEV), B, T, past, kc, vc, S_max)
+        psum += part.double().cpu()
+        attn.append(f64(a))
+    oc1 = O.unsharded(ocfg(w, 0))
+    Wc = {k: synth.to_f64(v) for k, v in W.items()}
+    kc1 = np.zeros((B, w["n_kv_heads"], S_max, 128))
+    ref = O.qkv_attn(oc1, synth.to_f64(x), B, T, past, O.merge_qkv(Wc["q"], Wc["k"], Wc["v"]), Wc["q_norm"],
+                     Wc["k_norm"], Wc["o"], kc1, kc1.copy(), store=lambda v: np.asarray(v, np.float64))
+    assert relerr(np.concatenate(attn, 1), ref["attn"]) <= TOL_BF16
+    assert relerr(psum.numpy(), ref["partial"]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("wid", [2, 4, 5])
+@pytest.mark.parametrize("phase", ["prefill", "decode"])
+def test_qkv_attn_full_size_sampled(wid, phase):
+    w = synth.WORKLOADS[wid]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    if phase == "prefill":
+        B, T, past = 1, w["prefill_T"], 0
+        S_max = T
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, T - 1], np.random.default_rng(T).integers(0, T, 11)]))
+    else:
+        B, T, past = w["decode_B"], 1, w["decode_ctx"] - 1
+        S_max = w["decode_ctx"]
+        rows = np.unique(np.concatenate([[0, B - 1], np.random.default_rng(B).integers(0, B, 6)]))
+    ranks = [0, 1]
+    out = {}
+    for r in ranks:
+        rk, kc, vc, part = check_attn(w, wid, r, B, T, past, S_max, rows=rows, Wg=Wg, W=W)
+        out[r] = (rk.L.kv_head0, kc.cpu(), vc.cpu())
+    if wid == 5:   # ranks 0 and 1 hold replicas of kv head 0: bit-identical caches
+        assert out[0][0] == out[1][0] == 0
+        assert torch.equal(out[0][1].view(torch.int16), out[1][1].view(torch.int16))
+        assert torch.equal(out[0][2].view(torch.int16), out[1][2].view(torch.int16))
+
+
+def test_deterministic_reruns():
+    w, wid = MID["rep2"], MID_WID["rep2"]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    rk = Rank(w, 1, Wg)
+    x = synth.activations(wid, 130, w["hidden"]).to(DEV)
+    outs = []
+    for _ in range(2):
+        kc, vc, _, _ = make_cache(w, wid, rk, 2, 80, 10, w["n_kv_heads"])
+        q, a, part = run_attn(rk, x, 2, 65, 10, kc, vc, 80)
+        h, mp = run_mlp(rk, x, 130)
+        outs.append([t.clone() for t in (q, a, part, kc, vc, h, mp)])
+    for t1, t2 in zip(*outs):
+        assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
