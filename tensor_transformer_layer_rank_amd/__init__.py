@@ -72,7 +72,13 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run python -m tensor_transformer_layer_rank_amd.build")
+        # The tensors handed to the library belong to torch's HIP runtime, so
+        # the library must bind to that same runtime: torch is loaded first,
+        # and its libamdhip64 (soname libamdhip64.so.7) then satisfies the
+        # library's dependency.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
+        _check_single_hip_runtime()
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         C = ctypes.POINTER(tp_cfg)
         L.tp_local_dims.argtypes = [C, ctypes.POINTER(tp_local)]
@@ -89,6 +95,16 @@ def lib() -> ctypes.CDLL:
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def _check_single_hip_runtime():
+    try:
+        maps = open("/proc/self/maps").read().splitlines()
+    except OSError:
+        return
+    paths = {os.path.realpath(l.split()[-1]) for l in maps if "libamdhip64" in l and "/" in l}
+    if len(paths) > 1:
+        raise RuntimeError(f"two HIP runtimes are loaded ({sorted(paths)}); import torch before loading libtpshard")
 
 
 def _check(st: int):
