@@ -31,16 +31,33 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 // land on 16 distinct 16-byte slots of the 256-byte bank space.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Buffer descriptor over [base, base + bytes): loads past the end return
+// zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n, 0x00020000);
+}
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes go straight to LDS at
+// lds_base + 16 * lane (lds_base is wave-uniform), no VGPR staging.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
 template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M>
-__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
+__global__ __launch_bounds__(WGM * WGN * 64)
+__attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN >= 65536 ? WGM * WGN / 4 : 2))) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                               int64_t k_per_split) {
   constexpr int BK = 64;
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int KC = BK / 8;
-  constexpr int A_LD = BM * KC / NT, B_LD = BN * KC / NT;
-  static_assert(BM * KC % NT == 0 && BN * KC % NT == 0, "tile/threads mismatch");
+  constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 block");
   static_assert(EPI != EPI_SILU_BF16 || (TN % 2 == 0), "silu pairs need an even number of n-blocks");
   constexpr int STAGE = (BM + BN) * BK;
@@ -70,62 +87,90 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmProblem p, int
   }
   const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
 
-  // global row of B for tile row n (-1 = outside the matrix)
-  auto b_row = [&](int n) -> int64_t {
+  // Tile loads.  Wave w fills 8-row groups g = w, w + NW, ... of each
+  // stage; lane l of a group writes LDS row 8g + l/8, physical chunk l%8,
+  // and so fetches the logical chunk that the swizzle puts there.  Sources
+  // are buffer descriptors over the tile's rows of A and B, advanced by k0
+  // per block; rows past the matrix fall outside the descriptor (they only
+  // feed outputs that are never stored).
+  constexpr int NW = WGM * WGN;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "8-row groups must split evenly");
+  static_assert(EPI != EPI_SILU_BF16 || (BN / 2) % 8 == 0, "gate/up halves must hold whole groups");
+  constexpr int A_G = BM / (8 * NW), B_G = BN / (8 * NW);
+  const int grow = lane >> 3, gpc = lane & 7;
+  const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
+  // B rows of this tile: [b_row0, +BN) or, for silu, [gate0, +BN/2) and [up0, +BN/2)
+  const int64_t nrow0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) : (int64_t)tn * BN;
+  const int64_t nrows = EPI == EPI_SILU_BF16 ? p.li - nrow0 : p.N - nrow0;
+  const bf16* a_base = p.A + m0 * p.lda;
+  const bf16* b_base = p.B + nrow0 * p.ldb;
+  const bf16* u_base = p.B + (p.li + nrow0) * p.ldb;   // silu only
+  // lane offset inside a group's 8 rows (bytes), with the swizzled chunk
+  auto goff = [&](int row, int64_t ld_b) -> uint32_t {
+    return (uint32_t)(row * ld_b + ((gpc ^ ((row >> 1) & 7)) << 4));
+  };
+  auto dma_block = [&](int64_t k0, int buf) {
+    bf16* sA = smem + buf * STAGE;
+    bf16* sB = sA + BM * BK;
+    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(a_base + k0, (M - m0) * lda_b - k0 * 2);
+#pragma unroll
+    for (int i = 0; i < A_G; ++i) {
+      const int g = wave + i * NW;
+      dma16(ra_, goff(g * 8 + grow, lda_b), sA + g * 8 * BK);
+    }
     if (EPI == EPI_SILU_BF16) {
-      const int half = n / (BN / 2);
-      const int64_t hcol = (int64_t)tn * (BN / 2) + (n - half * (BN / 2));
-      return hcol < p.li ? half * p.li + hcol : -1;
-    }
-    const int64_t r = (int64_t)tn * BN + n;
-    return r < p.N ? r : -1;
-  };
-
-  // per-thread global source pointers (fixed over k); nullptr = zero fill
-  const bf16* a_src[A_LD];
-  const bf16* b_src[B_LD];
+      const __amdgpu_buffer_rsrc_t rg = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
+      const __amdgpu_buffer_rsrc_t ru = make_rsrc(u_base + k0, nrows * ldb_b - k0 * 2);
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int q = tid + i * NT, row = q / KC, ch = q % KC;
-    const int64_t gm = m0 + row;
-    a_src[i] = gm < M ? p.A + gm * p.lda + ch * 8 : nullptr;
-  }
+      for (int i = 0; i < B_G; ++i) {
+        const int g = wave + i * NW;
+        const bool up = g * 8 >= BN / 2;
+        dma16(up ? ru : rg, goff(g * 8 + grow - (up ? BN / 2 : 0), ldb_b) , sB + g * 8 * BK);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int q = tid + i * NT, row = q / KC, ch = q % KC;
-    const int64_t gr = b_row(row);
-    b_src[i] = gr >= 0 ? p.B + gr * p.ldb + ch * 8 : nullptr;
-  }
-
-  u32x4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int ch = (tid + i * NT) % KC;
-      const bool ok = a_src[i] && (k0 + ch * 8 < kend);
-      ra[i] = ok ? *reinterpret_cast<const u32x4*>(a_src[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int ch = (tid + i * NT) % KC;
-      const bool ok = b_src[i] && (k0 + ch * 8 < kend);
-      rb[i] = ok ? *reinterpret_cast<const u32x4*>(b_src[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < B_G; ++i) {
+        const int g = wave + i * NW;
+        dma16(rb_, goff(g * 8 + grow, ldb_b), sB + g * 8 * BK);
+      }
     }
   };
-  auto sstore = [&](int buf) {
+  // last, partial K block: through registers; chunks at or past kend are
+  // replaced by zeros
+  u32x4 ra[A_G], rb[B_G];
+  auto reg_load = [&](int64_t k0) {
+    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(a_base + k0, (M - m0) * lda_b - k0 * 2);
+#pragma unroll
+    for (int i = 0; i < A_G; ++i) {
+      const int row = (wave + i * NW) * 8 + grow;
+      const bool ok = k0 + ((gpc ^ ((row >> 1) & 7)) << 3) < kend;
+      const u32x4 v = load16(ra_, goff(row, lda_b));
+      ra[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(u_base + k0, nrows * ldb_b - k0 * 2);
+#pragma unroll
+    for (int i = 0; i < B_G; ++i) {
+      const int n = (wave + i * NW) * 8 + grow;
+      const bool up = EPI == EPI_SILU_BF16 && n >= BN / 2;
+      const int nn = up ? n - BN / 2 : n;
+      const bool ok = k0 + ((gpc ^ ((n >> 1) & 7)) << 3) < kend;
+      const u32x4 v = load16(up ? ru : rg, goff(nn, ldb_b));
+      rb[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto reg_store = [&](int buf) {
     bf16* sA = smem + buf * STAGE;
     bf16* sB = sA + BM * BK;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + i * NT, row = q / KC, ch = q % KC;
-      *reinterpret_cast<u32x4*>(sA + row * BK + swz(row, ch) * 8) = ra[i];
-    }
+    for (int i = 0; i < A_G; ++i)
+      *reinterpret_cast<u32x4*>(sA + (wave + i * NW) * 8 * BK + lane * 8) = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int q = tid + i * NT, row = q / KC, ch = q % KC;
-      *reinterpret_cast<u32x4*>(sB + row * BK + swz(row, ch) * 8) = rb[i];
-    }
+    for (int i = 0; i < B_G; ++i)
+      *reinterpret_cast<u32x4*>(sB + (wave + i * NW) * 8 * BK + lane * 8) = rb[i];
   };
+  auto full_block = [&](int kt) { return kbeg + (int64_t)(kt + 1) * BK <= kend; };
   // tile-local column of the j-th 32-wide n-block of this wave
   auto ncol = [&](int j) -> int {
     if (EPI == EPI_SILU_BF16)
@@ -141,77 +186,167 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmProblem p, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  if (nk > 0) {
-    gload(kbeg);
-    sstore(0);
-    __syncthreads();
-  }
   const int lr = lane & 31, lh = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kbeg + (int64_t)(kt + 1) * BK);
+  bf16x8 af[2][TM], bfr[2][TN];
+  // One K block from LDS stage `cur`, written in issue order and fenced so
+  // the compiler keeps it: per k-step, MFMAs go out two at a time, each pair
+  // followed by one operand read for the next k-step and, every other pair,
+  // one slice of the next block's direct-to-LDS loads.  LDS latency and the
+  // texture path then overlap the matrix pipe instead of taking turns.
+  constexpr int KS = BK / 16;
+  constexpr int NF = TM + TN, NMF = TM * TN, NV = A_G + B_G;
+  constexpr int NPAIR = (NMF + 1) / 2;
+  constexpr int RDP = (NF + NPAIR - 1) / NPAIR;   // operand reads after each MFMA pair
+  auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int buf, int x) {
+    // order A0, B0..B(TN-1), A1..A(TM-1): the next k-step's first MFMAs
+    // need A0 with every B
+    const int c = ks * 2 + lh;
+    if (x == 0 || x > TN) {
+      const int i = x == 0 ? 0 : x - TN;
+      const int row = wm * WM + i * 32 + lr;
+      af[buf][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
+    } else {
+      const int row = ncol(x - 1) + lr;
+      bfr[buf][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
+    }
+  };
+  auto compute = [&](int cur, bool dma, int64_t next_k0) {
     const bf16* sA = smem + cur * STAGE;
     const bf16* sB = sA + BM * BK;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks * 2 + lh;
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + lr;
-        af[i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = ncol(j) + lr;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    bf16* nA = smem + (cur ^ 1) * STAGE;
+    bf16* nB = nA + BM * BK;
+    __amdgpu_buffer_rsrc_t ra_, rg, ru;
+    if (dma) {
+      ra_ = make_rsrc(a_base + next_k0, (M - m0) * lda_b - next_k0 * 2);
+      rg = make_rsrc(b_base + next_k0, nrows * ldb_b - next_k0 * 2);
+      ru = make_rsrc(u_base + next_k0, nrows * ldb_b - next_k0 * 2);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    auto dma_slice = [&](int v) {
+      if (v < A_G) {
+        const int g = wave + v * NW;
+        dma16(ra_, goff(g * 8 + grow, lda_b), nA + g * 8 * BK);
+      } else {
+        const int g = wave + (v - A_G) * NW;
+        const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
+        dma16(up ? ru : rg, goff(g * 8 + grow - (up ? BN / 2 : 0), ldb_b), nB + g * 8 * BK);
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < NF; ++x) read_frag(sA, sB, 0, 0, x);
+    __builtin_amdgcn_sched_barrier(0);
+    int v = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int pr = 0; pr < NPAIR; ++pr) {
+#pragma unroll
+        for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m)
+          acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][m / TN], bfr[ks & 1][m % TN],
+                                                                      acc[m / TN][m % TN], 0, 0, 0);
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
+        }
+        // spread the NV loads evenly over the KS * NPAIR pairs
+        if (dma && v < NV && (ks * NPAIR + pr + 1) * NV >= (v + 1) * KS * NPAIR) dma_slice(v++);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (dma)
+      while (v < NV) dma_slice(v++);
+  };
+
+  if (nk > 0) {
+    if (full_block(0)) {
+      dma_block(kbeg, 0);
+      wait_vm0();
+    } else {
+      reg_load(kbeg);
+      reg_store(0);
+    }
+    __syncthreads();
+  }
+  // iterations whose next block is a full one: DMA interleaved with compute
+  const bool tail = (kend - kbeg) % BK != 0;
+  const int n_dma = nk >= 2 ? nk - 2 + (tail ? 0 : 1) : 0;
+  int kt = 0;
+  for (; kt < n_dma; ++kt) {
+    compute(kt & 1, true, kbeg + (int64_t)(kt + 1) * BK);
+    wait_vm0();
+    __syncthreads();
+  }
+  // the rest: the next block (if any) is the partial last one
+  for (; kt < nk; ++kt) {
+    const bool next = kt + 1 < nk;
+    if (next) reg_load(kbeg + (int64_t)(kt + 1) * BK);
+    compute(kt & 1, false, 0);
+    if (next) reg_store((kt & 1) ^ 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
-  if (EPI == EPI_SILU_BF16) {
-    bf16* C = static_cast<bf16*>(p.C);
-#pragma unroll
-    for (int j = 0; j < TN / 2; ++j) {
-      const int64_t hcol = (int64_t)tn * (BN / 2) + wn * (WN / 2) + j * 32 + lr;
-      if (hcol >= p.li) continue;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t gm = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          if (gm < M) {
-            const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
-            C[gm * p.ldc + hcol] = f2bf(g / (1.f + __expf(-g)) * u);
-          }
-        }
-    }
-  } else {
+  // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
+  // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block.
+  if (EPI == EPI_F32) {
+    float* C = static_cast<float*>(p.C) + (SPLIT ? (int64_t)blockIdx.y * M * p.ldc : 0);
+    const bool full = m0 + BM <= M && (int64_t)(tn + 1) * BN <= p.N;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t gn = (int64_t)tn * BN + ncol(j) + lr;
-      if (gn >= p.N) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t gm = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          if (gm >= M) continue;
-          if (EPI == EPI_BF16) {
-            static_cast<bf16*>(p.C)[gm * p.ldc + gn] = f2bf(acc[i][j][e]);
-          } else {
-            float* C = static_cast<float*>(p.C) + (SPLIT ? (int64_t)blockIdx.y * M * p.ldc : 0);
-            C[gm * p.ldc + gn] = acc[i][j][e];
-          }
+          if (full || (gm < M && gn < p.N)) C[gm * p.ldc + gn] = acc[i][j][e];
         }
+    }
+    return;
+  }
+  // bf16 outputs: each wave stages its tile in LDS (row-major, 16-byte
+  // chunks XOR-swizzled by row), then writes whole 16-byte row chunks.
+  constexpr int OC = EPI == EPI_SILU_BF16 ? WN / 2 : WN;     // output columns per wave
+  constexpr int OCH = OC / 8;                                // 16-byte chunks per staged row
+  static_assert(WM * OC * 2 * WGM * WGN <= 2 * STAGE * 2, "staging does not fit");
+  bf16* so = smem + wave * (WM * OC);
+  auto so_idx = [&](int r, int c) { return r * OC + (((c >> 3) ^ (r & (OCH - 1))) << 3) + (c & 7); };
+  if (EPI == EPI_SILU_BF16) {
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
+          so[so_idx(i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), j * 32 + lr)] = f2bf(g / (1.f + __expf(-g)) * u);
+        }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          so[so_idx(i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), j * 32 + lr)] = f2bf(acc[i][j][e]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+  const int64_t ncols = EPI == EPI_SILU_BF16 ? p.li : p.N;
+  const int64_t col0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) + wn * (WN / 2) : (int64_t)tn * BN + wn * WN;
+  const int64_t row0 = m0 + wm * WM;
+  bf16* C = static_cast<bf16*>(p.C);
+  const bool vec = (p.ldc % 8) == 0;
+#pragma unroll 4
+  for (int q = lane; q < WM * OCH; q += 64) {
+    const int r = q / OCH, c = q % OCH;
+    const int64_t gm = row0 + r, gc = col0 + c * 8;
+    if (gm >= M || gc >= ncols) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * OC + ((c ^ (r & (OCH - 1))) << 3));
+    if (vec && gc + 8 <= ncols) {
+      *reinterpret_cast<u32x4*>(C + gm * p.ldc + gc) = v;
+    } else {
+      const bf16* e = reinterpret_cast<const bf16*>(&v);
+      for (int t = 0; t < 8 && gc + t < ncols; ++t) C[gm * p.ldc + gc + t] = e[t];
     }
   }
 }
@@ -365,7 +500,7 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
   const bool can_split = scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
   const Plan pl = make_plan(p.M, p.N, p.K, epi, can_split);
   switch (pl.tile) {
-    case TILE_256x256: return launch_tile<256, 256, 2, 2>(p, epi, pl, scratch, s);
+    case TILE_256x256: return launch_tile<256, 256, 4, 2>(p, epi, pl, scratch, s);
     case TILE_128x128: return launch_tile<128, 128, 2, 2>(p, epi, pl, scratch, s);
     case TILE_64x128: return launch_tile<64, 128, 2, 2>(p, epi, pl, scratch, s);
     default: return launch_tile<128, 64, 4, 1>(p, epi, pl, scratch, s);
