@@ -157,7 +157,8 @@ def run_bench(args):
     del src, full
     ws_attn_p = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_ATTN, 1, T, 0), dtype=torch.uint8, device=dev)
     ws_attn_d = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_ATTN, B, 1, ctx - 1), dtype=torch.uint8, device=dev)
-    ws_mlp = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_MLP, max(T, B), 1), dtype=torch.uint8, device=dev)
+    ws_mlp = torch.empty(max(tp.tp_workspace_bytes(c, tp.TP_OP_MLP, T, 1), tp.tp_workspace_bytes(c, tp.TP_OP_MLP, B, 1)),
+                         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     kinds = ((tp.TP_W_Q, "q", "qkv"), (tp.TP_W_K, "k", "qkv"), (tp.TP_W_V, "v", "qkv"), (tp.TP_W_O, "o", "o"),

@@ -18,9 +18,8 @@ namespace tps {
 
 namespace {
 
-constexpr int kKeysPerIter = 4;   // rows in flight per worker per iteration
-constexpr int kMinKeysPerSplit = 256;
-constexpr int kTargetBlocks = 2048;
+constexpr int kMinKeysPerSplit = 512;
+constexpr int kTargetBlocks = 256;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -45,18 +44,34 @@ __device__ __forceinline__ void unpack8(const u32x4& r, float* f) {
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// reinterpret one 32-bit word as a bf16 pair (the word arrives by value:
+// bit_cast applied directly to an element of a vector type is not reliable)
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
 // weight of a state with max m inside a merge whose max is M (0 for empty)
 __device__ __forceinline__ float lse_w(float m, float M) { return m == -INFINITY ? 0.f : ex2(m - M); }
 
-template <int REP>
+// REP q heads share a kv head; HS blocks split them (RH = REP / HS heads
+// each) and read the same K/V rows -- the HS blocks of one item are placed
+// on one XCD back to back, so all but the first read hit that XCD's L2.
+template <int REP, int HS>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit, int keys_per_split,
                                                           float qscale) {
-  __shared__ float s_o[4][REP][128];
-  __shared__ float s_ml[4][REP][2];
-  const int item = blockIdx.x;
+  constexpr int RH = REP / HS;
+  __shared__ float s_o[4][RH][128];
+  __shared__ float s_ml[4][RH][2];
+  int item, hs;
+  {
+    const int bid = blockIdx.x, xcd = bid % 8, j = bid / 8;
+    const int nitems = gridDim.x / HS;          // gridDim.x = items * HS, items % 8 == 0 when HS > 1
+    item = HS == 1 ? bid : (j / HS) * 8 + xcd;
+    hs = HS == 1 ? 0 : j % HS;
+    (void)nitems;
+  }
   const int split = item % nsplit;
   const int bk = item / nsplit;
   const int kvh = bk % a.lkv, b = bk / a.lkv;
+  const int h0 = kvh * REP + hs * RH;            // first q head of this block
   const int S = a.past + 1;
   const int s0 = split * keys_per_split;
   const int s1 = min(S, s0 + keys_per_split);
@@ -64,17 +79,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
   const int l16 = lane & 15;
   const int worker = wave * 4 + (lane >> 4);
 
-  float q[REP][8];
+  // q stays packed (bf16 pairs); q.k uses v_dot2_f32_bf16 on the packed K row
+  bf16x2 q2[RH][4];
 #pragma unroll
-  for (int h = 0; h < REP; ++h) {
-    const bf16* qp = a.q + (int64_t)b * a.lq * 128 + (int64_t)(kvh * REP + h) * 128 + l16 * 8;
-    unpack8(*reinterpret_cast<const u32x4*>(qp), q[h]);
+  for (int h = 0; h < RH; ++h) {
+    const bf16* qp = a.q + (int64_t)b * a.lq * 128 + (int64_t)(h0 + h) * 128 + l16 * 8;
+    const u32x4 r = *reinterpret_cast<const u32x4*>(qp);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[h][i] *= qscale;
+    for (int i = 0; i < 4; ++i) q2[h][i] = as_bf16x2(r[i]);
   }
-  float m[REP], l[REP], o[REP][8];
+  float m[RH], l[RH], o[RH][8];
 #pragma unroll
-  for (int h = 0; h < REP; ++h) {
+  for (int h = 0; h < RH; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
 #pragma unroll
@@ -84,37 +100,47 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
   const bf16* kb = a.k_cache + slab;
   const bf16* vb = a.v_cache + slab;
 
-  for (int s = s0 + worker; s < s1; s += 16 * kKeysPerIter) {
-    u32x4 kr[kKeysPerIter], vr[kKeysPerIter];
+  // Branch-free streaming, one stage of U rows per worker ahead: while a
+  // stage is scored, the next stage's K/V rows are already in flight.  Rows
+  // past the split are clamped to its last row and their scores masked.
+  constexpr int U = 4;
+  const int n_it = (s1 - s0 + 16 * U - 1) / (16 * U);
+  u32x4 kc[U], vc[U], kn[U], vn[U];
+  auto load_rows = [&](u32x4* kk, u32x4* vv, int s) {
 #pragma unroll
-    for (int u = 0; u < kKeysPerIter; ++u) {
-      const int ss = s + 16 * u;
-      if (ss < s1) {
-        kr[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)ss * 128);
-        vr[u] = *reinterpret_cast<const u32x4*>(vb + (int64_t)ss * 128);
-      } else {
-        kr[u] = u32x4{0u, 0u, 0u, 0u};
-        vr[u] = kr[u];
-      }
+    for (int u = 0; u < U; ++u) {
+      const int ss = min(s + 16 * u, s1 - 1);
+      kk[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)ss * 128);
+      vv[u] = *reinterpret_cast<const u32x4*>(vb + (int64_t)ss * 128);
     }
-    float sc[kKeysPerIter][REP];
+  };
+  load_rows(kn, vn, s0 + worker);
+  for (int it = 0; it < n_it; ++it) {
+    const int s = s0 + worker + it * 16 * U;
 #pragma unroll
-    for (int u = 0; u < kKeysPerIter; ++u) {
-      float kf[8];
-      unpack8(kr[u], kf);
+    for (int u = 0; u < U; ++u) {
+      kc[u] = kn[u];
+      vc[u] = vn[u];
+    }
+    if (it + 1 < n_it) load_rows(kn, vn, s + 16 * U);
+    float sc[U][RH];
 #pragma unroll
-      for (int h = 0; h < REP; ++h) {
+    for (int u = 0; u < U; ++u) {
+      const bool valid = s + 16 * u < s1;
+#pragma unroll
+      for (int h = 0; h < RH; ++h) {
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d = fmaf(q[h][i], kf[i], d);
-        sc[u][h] = (s + 16 * u < s1) ? row16_sum(d) : -INFINITY;
+        for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(q2[h][i], as_bf16x2(kc[u][i]), d, false);
+        d = row16_sum(d) * qscale;
+        sc[u][h] = valid ? d : -INFINITY;
       }
     }
 #pragma unroll
-    for (int h = 0; h < REP; ++h) {
+    for (int h = 0; h < RH; ++h) {
       float mx = sc[0][h];
 #pragma unroll
-      for (int u = 1; u < kKeysPerIter; ++u) mx = fmaxf(mx, sc[u][h]);
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
       const float mn = fmaxf(m[h], mx);
       const float corr = lse_w(m[h], mn);
       l[h] *= corr;
@@ -123,11 +149,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
       m[h] = mn;
     }
 #pragma unroll
-    for (int u = 0; u < kKeysPerIter; ++u) {
+    for (int u = 0; u < U; ++u) {
       float vf[8];
-      unpack8(vr[u], vf);
+      unpack8(vc[u], vf);
 #pragma unroll
-      for (int h = 0; h < REP; ++h) {
+      for (int h = 0; h < RH; ++h) {
         const float p = lse_w(sc[u][h], m[h]);
         l[h] += p;
 #pragma unroll
@@ -140,7 +166,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {
 #pragma unroll
-    for (int h = 0; h < REP; ++h) {
+    for (int h = 0; h < RH; ++h) {
       const float m2 = __shfl_xor(m[h], off, 64);
       const float l2 = __shfl_xor(l[h], off, 64);
       const float mn = fmaxf(m[h], m2);
@@ -153,7 +179,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
   }
   if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < REP; ++h) {
+    for (int h = 0; h < RH; ++h) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s_o[wave][h][l16 * 8 + i] = o[h][i];
       if (l16 == 0) {
@@ -163,7 +189,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
     }
   }
   __syncthreads();
-  for (int e = tid; e < REP * 128; e += 256) {
+  for (int e = tid; e < RH * 128; e += 256) {
     const int h = e / 128, d = e % 128;
     float M = -INFINITY;
 #pragma unroll
@@ -176,12 +202,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int nsplit
       O += s_o[w][h][d] * wt;
     }
     if (nsplit == 1) {
-      a.out[(int64_t)b * a.lq * 128 + (int64_t)(kvh * REP + h) * 128 + d] = f2bf(L > 0.f ? O / L : 0.f);
+      a.out[(int64_t)b * a.lq * 128 + (int64_t)(h0 + h) * 128 + d] = f2bf(L > 0.f ? O / L : 0.f);
     } else {
-      const int64_t base = (int64_t)item * REP + h;
+      const int64_t base = (int64_t)item * REP + hs * RH + h;
       a.scratch[base * 128 + d] = O;
       if (d == 0) {
-        float* ml = a.scratch + (int64_t)gridDim.x * REP * 128;
+        float* ml = a.scratch + (int64_t)(gridDim.x / HS) * REP * 128;
         ml[base * 2] = M;
         ml[base * 2 + 1] = L;
       }
@@ -213,6 +239,9 @@ __global__ __launch_bounds__(256) void attn_decode_combine(AttnArgs a, int nspli
   }
 }
 
+// One split per (b, kv head) while that already gives about one block per
+// CU: a block then streams its whole slab and no merge pass is needed.
+// Smaller grids split the keys (at least kMinKeysPerSplit per split).
 void split_plan(int B, int lkv, int S, int& nsplit, int& kps) {
   const int items = B * lkv;
   int ns = (kTargetBlocks + items - 1) / items;
@@ -223,7 +252,7 @@ void split_plan(int B, int lkv, int S, int& nsplit, int& kps) {
   nsplit = (S + kps - 1) / kps;    // every split holds at least one key
 }
 
-template <int REP>
+template <int REP, int HS>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int S = a.past + 1;
   int nsplit, kps;
@@ -231,7 +260,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
   const int items = a.B * a.lkv * nsplit;
   // 1/sqrt(128) with log2(e) folded in: scores are in the exp2 domain
   const float qscale = 0.08838834764831845f * 1.4426950408889634f;
-  attn_decode_kernel<REP><<<items, 256, 0, s>>>(a, nsplit, kps, qscale);
+  if (HS > 1 && items % 8 != 0) return launch<REP, 1>(a, s);
+  attn_decode_kernel<REP, HS><<<items * HS, 256, 0, s>>>(a, nsplit, kps, qscale);
   if (nsplit > 1) {
     const int64_t total = (int64_t)a.B * a.lq * 128;
     int64_t g = (total + 255) / 256;
@@ -254,11 +284,11 @@ size_t attn_decode_scratch_bytes(int B, int lq, int lkv, int ctx) {
 hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   switch (a.lq / a.lkv) {
-    case 1: return launch<1>(a, s);
-    case 2: return launch<2>(a, s);
-    case 4: return launch<4>(a, s);
-    case 8: return launch<8>(a, s);
-    case 16: return launch<16>(a, s);
+    case 1: return launch<1, 1>(a, s);
+    case 2: return launch<2, 1>(a, s);
+    case 4: return launch<4, 1>(a, s);
+    case 8: return launch<8, 2>(a, s);
+    case 16: return launch<16, 4>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -377,13 +377,17 @@ def check_attn(w, wid, r, B, T, past, S_max, rows=None, Wg=None, W=None, tol=TOL
 
 
 @pytest.mark.parametrize("name", list(MID))
-@pytest.mark.parametrize("phase", ["prefill", "prefill-after-past", "decode", "decode-ctx1"])
+@pytest.mark.parametrize("phase", ["prefill", "prefill-after-past", "decode", "decode-ctx1", "decode-long"])
 def test_qkv_attn_mid(name, phase):
+    """decode: 8 sequences (head-split blocks when rep >= 8); decode-ctx1:
+    3 sequences, one key; decode-long: 2 sequences at context 3000, which
+    splits the keys and merges the splits."""
     w, wid = MID[name], MID_WID[name]
     W = synth.full_weights(wid, w)
     Wg = {k: v.to(DEV) for k, v in W.items()}
     B, T, past, S_max = {"prefill": (2, 300, 0, 320), "prefill-after-past": (2, 77, 150, 240),
-                         "decode": (5, 1, 299, 310), "decode-ctx1": (3, 1, 0, 4)}[phase]
+                         "decode": (8, 1, 299, 310), "decode-ctx1": (3, 1, 0, 4),
+                         "decode-long": (2, 1, 2999, 3000)}[phase]
     for r in range(w["tp"]):
         check_attn(w, wid, r, B, T, past, S_max, Wg=Wg, W=W)
 
