@@ -12,6 +12,8 @@
 // operand read touches hit distinct banks); workgroup ids remapped so that
 // each of the 8 XCDs (fed round-robin by the dispatcher) works on a
 // contiguous, M-grouped range of tiles and shares A/B panels in its own L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tps {
@@ -48,11 +50,27 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// LDS stages per tile shape: as many as let two workgroups share a CU's
+// 160 KB (at least 2, at most 6) -- a second workgroup hides barrier and
+// load stalls better than a deeper ring
+constexpr int gemm_stages(int bm, int bn) {
+  return (81920 / ((bm + bn) * 64 * 2)) > 6 ? 6 : ((81920 / ((bm + bn) * 64 * 2)) < 2 ? 2 : 81920 / ((bm + bn) * 64 * 2));
+}
+// waves per SIMD that one CU holds for a tile shape (LDS-limited)
+constexpr int gemm_waves_per_simd(int bm, int bn, int nw) {
+  return (nw / 4 < 1 ? 1 : nw / 4) * (163840 / (gemm_stages(bm, bn) * (bm + bn) * 64 * 2));
+}
 
 template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M>
 __global__ __launch_bounds__(WGM * WGN * 64)
-__attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN >= 65536 ? WGM * WGN / 4 : 2))) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
-                                                              int64_t k_per_split) {
+__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd(BM, BN, WGM * WGN), gemm_waves_per_simd(BM, BN, WGM * WGN))))
+void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int BK = 64;
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -61,7 +79,9 @@ __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 block");
   static_assert(EPI != EPI_SILU_BF16 || (TN % 2 == 0), "silu pairs need an even number of n-blocks");
   constexpr int STAGE = (BM + BN) * BK;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+  constexpr int S = gemm_stages(BM, BN);     // LDS ring: blocks in flight = S - 1
+  static_assert(S >= 2, "need at least double buffering");
+  __shared__ __attribute__((aligned(16))) bf16 smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -109,6 +129,7 @@ __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN
   auto goff = [&](int row, int64_t ld_b) -> uint32_t {
     return (uint32_t)(row * ld_b + ((gpc ^ ((row >> 1) & 7)) << 4));
   };
+  // one whole K block into LDS stage `buf` (prologue)
   auto dma_block = [&](int64_t k0, int buf) {
     bf16* sA = smem + buf * STAGE;
     bf16* sB = sA + BM * BK;
@@ -118,59 +139,25 @@ __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN
       const int g = wave + i * NW;
       dma16(ra_, goff(g * 8 + grow, lda_b), sA + g * 8 * BK);
     }
-    if (EPI == EPI_SILU_BF16) {
-      const __amdgpu_buffer_rsrc_t rg = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
-      const __amdgpu_buffer_rsrc_t ru = make_rsrc(u_base + k0, nrows * ldb_b - k0 * 2);
-#pragma unroll
-      for (int i = 0; i < B_G; ++i) {
-        const int g = wave + i * NW;
-        const bool up = g * 8 >= BN / 2;
-        dma16(up ? ru : rg, goff(g * 8 + grow - (up ? BN / 2 : 0), ldb_b) , sB + g * 8 * BK);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
-#pragma unroll
-      for (int i = 0; i < B_G; ++i) {
-        const int g = wave + i * NW;
-        dma16(rb_, goff(g * 8 + grow, ldb_b), sB + g * 8 * BK);
-      }
-    }
-  };
-  // last, partial K block: through registers; chunks at or past kend are
-  // replaced by zeros
-  u32x4 ra[A_G], rb[B_G];
-  auto reg_load = [&](int64_t k0) {
-    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(a_base + k0, (M - m0) * lda_b - k0 * 2);
-#pragma unroll
-    for (int i = 0; i < A_G; ++i) {
-      const int row = (wave + i * NW) * 8 + grow;
-      const bool ok = k0 + ((gpc ^ ((row >> 1) & 7)) << 3) < kend;
-      const u32x4 v = load16(ra_, goff(row, lda_b));
-      ra[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(u_base + k0, nrows * ldb_b - k0 * 2);
 #pragma unroll
     for (int i = 0; i < B_G; ++i) {
-      const int n = (wave + i * NW) * 8 + grow;
-      const bool up = EPI == EPI_SILU_BF16 && n >= BN / 2;
-      const int nn = up ? n - BN / 2 : n;
-      const bool ok = k0 + ((gpc ^ ((n >> 1) & 7)) << 3) < kend;
-      const u32x4 v = load16(up ? ru : rg, goff(nn, ldb_b));
-      rb[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      const int g = wave + i * NW;
+      const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
+      dma16(up ? ru : rg, goff(g * 8 + grow - (up ? BN / 2 : 0), ldb_b), sB + g * 8 * BK);
     }
   };
-  auto reg_store = [&](int buf) {
-    bf16* sA = smem + buf * STAGE;
-    bf16* sB = sA + BM * BK;
-#pragma unroll
-    for (int i = 0; i < A_G; ++i)
-      *reinterpret_cast<u32x4*>(sA + (wave + i * NW) * 8 * BK + lane * 8) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_G; ++i)
-      *reinterpret_cast<u32x4*>(sB + (wave + i * NW) * 8 * BK + lane * 8) = rb[i];
+  // The last block may end inside the 64-wide K window: its columns at or
+  // past kend were loaded from the next row (or read as zero past the
+  // matrix) and are cleared here, after the block has landed.
+  auto zero_tail = [&](int buf, int64_t k0) {
+    bf16* st = smem + buf * STAGE;
+    for (int q = tid; q < (BM + BN) * KC; q += NT) {
+      const int row = q / KC, lc = q % KC;
+      if (k0 + lc * 8 >= kend) *reinterpret_cast<u32x4*>(st + row * BK + swz(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  auto full_block = [&](int kt) { return kbeg + (int64_t)(kt + 1) * BK <= kend; };
   // tile-local column of the j-th 32-wide n-block of this wave
   auto ncol = [&](int j) -> int {
     if (EPI == EPI_SILU_BF16)
@@ -210,13 +197,16 @@ __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN
       bfr[buf][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
     }
   };
-  auto compute = [&](int cur, bool dma, int64_t next_k0) {
+  // dma_tag: std::true_type when this iteration issues a later block's
+  // loads (compile-time, so the fenced stream has no branches)
+  auto compute = [&](auto dma_tag, int cur, int64_t next_k0, int next_buf) {
+    constexpr bool dma = decltype(dma_tag)::value;
     const bf16* sA = smem + cur * STAGE;
     const bf16* sB = sA + BM * BK;
-    bf16* nA = smem + (cur ^ 1) * STAGE;
+    bf16* nA = smem + next_buf * STAGE;
     bf16* nB = nA + BM * BK;
     __amdgpu_buffer_rsrc_t ra_, rg, ru;
-    if (dma) {
+    if constexpr (dma) {
       ra_ = make_rsrc(a_base + next_k0, (M - m0) * lda_b - next_k0 * 2);
       rg = make_rsrc(b_base + next_k0, nrows * ldb_b - next_k0 * 2);
       ru = make_rsrc(u_base + next_k0, nrows * ldb_b - next_k0 * 2);
@@ -249,40 +239,55 @@ __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN
           for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
         }
         // spread the NV loads evenly over the KS * NPAIR pairs
-        if (dma && v < NV && (ks * NPAIR + pr + 1) * NV >= (v + 1) * KS * NPAIR) dma_slice(v++);
+        if constexpr (dma) {
+          if (v < NV && (ks * NPAIR + pr + 1) * NV >= (v + 1) * KS * NPAIR) dma_slice(v++);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (dma)
+    if constexpr (dma) {
       while (v < NV) dma_slice(v++);
+    }
   };
 
-  if (nk > 0) {
-    if (full_block(0)) {
-      dma_block(kbeg, 0);
-      wait_vm0();
-    } else {
-      reg_load(kbeg);
-      reg_store(0);
-    }
-    __syncthreads();
-  }
-  // iterations whose next block is a full one: DMA interleaved with compute
+  // Pipeline: blocks 0 .. S-2 are issued up front; iteration kt computes
+  // stage kt % S while the loads of block kt + S - 1 go out between its
+  // MFMAs, then waits until block kt + 1 has landed (vmcnt counts this
+  // wave's outstanding loads, which complete in issue order).
+  constexpr int NVW = A_G + B_G;            // loads per block per wave
   const bool tail = (kend - kbeg) % BK != 0;
-  const int n_dma = nk >= 2 ? nk - 2 + (tail ? 0 : 1) : 0;
-  int kt = 0;
-  for (; kt < n_dma; ++kt) {
-    compute(kt & 1, true, kbeg + (int64_t)(kt + 1) * BK);
-    wait_vm0();
+  auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
+  auto settle = [&](int blk) {
     __syncthreads();
+    if (tail && blk == nk - 1) {
+      zero_tail(blk % S, kblk(blk));
+      __syncthreads();
+    }
+  };
+  if (nk > 0) {
+    const int pro = nk < S - 1 ? nk : S - 1;
+    for (int blk = 0; blk < pro; ++blk) dma_block(kblk(blk), blk);
+    if (pro - 1 == S - 2)
+      wait_vm<(S - 2) * NVW>();
+    else
+      wait_vm0();
+    settle(0);
   }
-  // the rest: the next block (if any) is the partial last one
+  // steady state: every iteration issues block kt + S - 1 and has exactly
+  // S - 2 blocks in flight behind block kt + 1
+  int kt = 0;
+  for (; kt + S - 1 < nk; ++kt) {
+    compute(std::true_type{}, kt % S, kblk(kt + S - 1), (kt + S - 1) % S);
+    wait_vm<(S - 2) * NVW>();
+    settle(kt + 1);
+  }
+  // drain: nothing left to issue
   for (; kt < nk; ++kt) {
-    const bool next = kt + 1 < nk;
-    if (next) reg_load(kbeg + (int64_t)(kt + 1) * BK);
-    compute(kt & 1, false, 0);
-    if (next) reg_store((kt & 1) ^ 1);
-    __syncthreads();
+    compute(std::false_type{}, kt % S, 0, 0);
+    if (kt + 1 < nk) {
+      wait_vm0();
+      settle(kt + 1);
+    }
   }
 
   // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
@@ -307,7 +312,7 @@ __attribute__((amdgpu_waves_per_eu(BM * BN >= 65536 ? WGM * WGN / 4 : 2, BM * BN
   // chunks XOR-swizzled by row), then writes whole 16-byte row chunks.
   constexpr int OC = EPI == EPI_SILU_BF16 ? WN / 2 : WN;     // output columns per wave
   constexpr int OCH = OC / 8;                                // 16-byte chunks per staged row
-  static_assert(WM * OC * 2 * WGM * WGN <= 2 * STAGE * 2, "staging does not fit");
+  static_assert(WM * OC * 2 * WGM * WGN <= S * STAGE * 2, "staging does not fit");
   bf16* so = smem + wave * (WM * OC);
   auto so_idx = [&](int r, int c) { return r * OC + (((c >> 3) ^ (r & (OCH - 1))) << 3) + (c & 7); };
   if (EPI == EPI_SILU_BF16) {
