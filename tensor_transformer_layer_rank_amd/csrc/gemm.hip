@@ -56,20 +56,20 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-// LDS stages per tile shape: as many as let two workgroups share a CU's
-// 160 KB (at least 2, at most 6) -- a second workgroup hides barrier and
-// load stalls better than a deeper ring
+// Default LDS stages per tile shape: as many as let two workgroups share a
+// CU's 160 KB (at least 2, at most 6).  Weight-streaming shapes (few rows)
+// pick deeper rings explicitly.
 constexpr int gemm_stages(int bm, int bn) {
   return (81920 / ((bm + bn) * 64 * 2)) > 6 ? 6 : ((81920 / ((bm + bn) * 64 * 2)) < 2 ? 2 : 81920 / ((bm + bn) * 64 * 2));
 }
-// waves per SIMD that one CU holds for a tile shape (LDS-limited)
-constexpr int gemm_waves_per_simd(int bm, int bn, int nw) {
-  return (nw / 4 < 1 ? 1 : nw / 4) * (163840 / (gemm_stages(bm, bn) * (bm + bn) * 64 * 2));
+// waves per SIMD that one CU holds for a tile shape and ring depth (LDS-limited)
+constexpr int gemm_waves_per_simd(int bm, int bn, int nw, int stages) {
+  return (nw / 4 < 1 ? 1 : nw / 4) * (163840 / (stages * (bm + bn) * 64 * 2));
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M, int S>
 __global__ __launch_bounds__(WGM * WGN * 64)
-__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd(BM, BN, WGM * WGN), gemm_waves_per_simd(BM, BN, WGM * WGN))))
+__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd(BM, BN, WGM * WGN, S), gemm_waves_per_simd(BM, BN, WGM * WGN, S))))
 void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int BK = 64;
   constexpr int NT = WGM * WGN * 64;
@@ -79,8 +79,8 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 block");
   static_assert(EPI != EPI_SILU_BF16 || (TN % 2 == 0), "silu pairs need an even number of n-blocks");
   constexpr int STAGE = (BM + BN) * BK;
-  constexpr int S = gemm_stages(BM, BN);     // LDS ring: blocks in flight = S - 1
-  static_assert(S >= 2, "need at least double buffering");
+  // LDS ring of S stages: S - 1 blocks in flight
+  static_assert(S >= 2 && S * STAGE * 2 <= 163840, "ring must be double-buffered and fit the CU's LDS");
   __shared__ __attribute__((aligned(16))) bf16 smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -257,11 +257,18 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int NVW = A_G + B_G;            // loads per block per wave
   const bool tail = (kend - kbeg) % BK != 0;
   auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
+  // A bare s_barrier, not __syncthreads(): the latter's workgroup release
+  // fence waits for every outstanding direct-to-LDS load (vmcnt(0)), which
+  // would collapse the ring to one block in flight.  The wait_vm<> before
+  // each settle already guarantees that this wave's loads of the next block
+  // have landed; the barrier makes that true for all waves.  The asm memory
+  // clobber keeps the compiler from moving LDS accesses across it.
   auto settle = [&](int blk) {
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");
     if (tail && blk == nk - 1) {
       zero_tail(blk % S, kblk(blk));
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zero stores are done
+      asm volatile("s_barrier" ::: "memory");
     }
   };
   if (nk > 0) {
@@ -314,6 +321,9 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int OCH = OC / 8;                                // 16-byte chunks per staged row
   static_assert(WM * OC * 2 * WGM * WGN <= S * STAGE * 2, "staging does not fit");
   bf16* so = smem + wave * (WM * OC);
+  // the staging area overlaps ring stages that slower waves may still be
+  // reading for the last K block
+  __syncthreads();
   auto so_idx = [&](int r, int c) { return r * OC + (((c >> 3) ^ (r & (OCH - 1))) << 3) + (c & 7); };
   if (EPI == EPI_SILU_BF16) {
 #pragma unroll
@@ -384,56 +394,83 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
 }
 
 // ---- tile-shape choice -----------------------------------------------------
+//
+// Each variant is a tile shape, a wave layout and an LDS ring depth.  The
+// planner prices every (variant, split) pair with a two-sided model and keeps
+// the cheapest:
+//   compute: rounds of resident workgroups x (K blocks x time per K block +
+//            output tile write), with the per-block times measured on this
+//            GPU at full load;
+//   memory:  weight bytes (+ fp32 split partials, written and read back) at
+//            the streaming rate, or at the per-workgroup rate when too few
+//            workgroups are resident to fill HBM;
+// plus a fixed cost per launch (a split adds the reduction launch).
+struct Variant {
+  int bm, bn, stages;
+  int resident;        // workgroups one CU holds (LDS-limited)
+  float t_kb_us;       // time per 64-wide K block per resident round at full load
+  bool silu;           // wave tile has an even number of 32-column blocks
+};
+enum VariantId { V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V_COUNT };
+constexpr Variant kVariants[V_COUNT] = {
+    {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.65f, true},
+    {128, 128, 2, 2, 1.20f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
+    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},
+};
+constexpr double kHbmBytesPerUs = 5.0e6;       // sustained weight streaming, bytes per microsecond
+constexpr double kWgBytesPerUs = 2.5e4;        // one workgroup's streaming rate
+constexpr double kLaunchUs = 4.0;
+constexpr double kEpiUsPerKB = 0.07;           // tile write-out per resident round
 
-enum TileCfg { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2, TILE_128x64 = 3, TILE_COUNT };
-struct TileShape { int bm, bn; float eff; };
-constexpr TileShape kShapes[TILE_COUNT] = {{256, 256, 1.0f}, {128, 128, 0.75f}, {64, 128, 0.5f}, {128, 64, 0.5f}};
+struct Plan { int v; int splits; int64_t kps; int tiles_m, tiles_n; };
 
-struct Plan { int tile; int splits; int64_t kps; int tiles_m, tiles_n; };
+double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int64_t splits, int64_t* tm_out,
+                 int64_t* tn_out) {
+  const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;
+  const int64_t bn_out = epi == EPI_SILU_BF16 && splits == 1 ? v.bn / 2 : v.bn;
+  const int64_t cols = splits == 1 ? ncols : N;   // split partials use the plain column order
+  const int64_t tm = (M + v.bm - 1) / v.bm, tn = (cols + bn_out - 1) / bn_out;
+  *tm_out = tm;
+  *tn_out = tn;
+  const int64_t wgs = tm * tn * splits;
+  const int64_t resident = (int64_t)kCUs * v.resident;
+  const int64_t rounds = (wgs + resident - 1) / resident;
+  const int64_t kb = (K / 64 + splits - 1) / splits + (K % 64 != 0);
+  const double out_kb = (double)v.bm * v.bn * (splits > 1 || epi == EPI_F32 ? 4 : 2) / 1024.0;
+  const double t_comp = rounds * (kb * v.t_kb_us + out_kb * kEpiUsPerKB);
+  const double partial = splits > 1 ? (double)splits * M * N * 4 : 0.0;
+  const double bytes = (double)N * K * 2 + (double)M * K * 2 + partial;
+  const double active = (double)(wgs < resident ? wgs : resident);
+  const double rate = active * kWgBytesPerUs < kHbmBytesPerUs ? active * kWgBytesPerUs : kHbmBytesPerUs;
+  const double t_mem = bytes / rate * ((double)rounds * resident / (wgs > resident ? wgs : resident));
+  // the reduction runs after the GEMM: it reads every partial and writes C
+  const double t_red = splits > 1 ? (partial + (double)M * ncols * (epi == EPI_F32 ? 4 : 2)) / kHbmBytesPerUs + kLaunchUs : 0.0;
+  return (t_comp > t_mem ? t_comp : t_mem) + kLaunchUs + t_red;
+}
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split) {
-  const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;   // output columns
-  Plan best{TILE_256x256, 1, K, 0, 0};
+  Plan best{V256x256, 1, K, 0, 0};
   double best_cost = 1e300;
-  for (int t = 0; t < TILE_COUNT; ++t) {
-    const TileShape s = kShapes[t];
-    const int64_t bn_out = epi == EPI_SILU_BF16 ? s.bn / 2 : s.bn;
-    const int64_t tm = (M + s.bm - 1) / s.bm, tn = (ncols + bn_out - 1) / bn_out;
-    const int64_t tiles = tm * tn;
-    const int64_t waves = (tiles + kCUs - 1) / kCUs;
-    const double cost = (double)waves * s.bm * s.bn / s.eff;
-    if (cost < best_cost * 0.999) {
-      best_cost = cost;
-      best = Plan{t, 1, K, (int)tm, (int)tn};
-    }
-  }
-  // Split K when the grid cannot fill the GPU and K is long enough to share.
-  const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
-  // fp32 partials cost splits*M*N*8 bytes of traffic against the N*K*2
-  // bytes of B, so the split count is capped at K / (8 M) (<= half of it).
-  if (allow_split && tiles < kCUs && K >= 512) {
-    int64_t splits = (2 * kCUs + tiles - 1) / tiles;
-    const int64_t kblocks = K / 64;
-    const int64_t cap = K / (8 * M);
-    if (splits > cap) splits = cap;
-    if (splits > kblocks) splits = kblocks;
-    if (splits > 1) {
-      // split-K re-reads nothing but writes fp32 partials; the tile is
-      // computed with the plain [gate; up] column order in that case
-      const int64_t kps = ((K / 64 + splits - 1) / splits) * 64;
-      splits = (K + kps - 1) / kps;
-      if (splits > 1) {
-        const TileShape s = kShapes[best.tile];
-        best.tiles_n = (int)((N + s.bn - 1) / s.bn);
-        best.splits = (int)splits;
-        best.kps = kps;
+  const int64_t kblocks = (K + 63) / 64;
+  for (int vi = 0; vi < V_COUNT; ++vi) {
+    const Variant& v = kVariants[vi];
+    for (int64_t sp = 1; sp <= 8; ++sp) {
+      if (sp > 1 && (!allow_split || kblocks < 8 * sp)) break;
+      if (epi == EPI_SILU_BF16 && sp == 1 && !v.silu) continue;
+      int64_t tm, tn;
+      // a split must win clearly: its partials also cost workspace
+      const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn) * (sp > 1 ? 1.05 : 1.0);
+      if (c < best_cost * 0.999) {
+        best_cost = c;
+        const int64_t kps = sp == 1 ? K : ((kblocks + sp - 1) / sp) * 64;
+        best = Plan{vi, sp == 1 ? 1 : (int)((K + kps - 1) / kps), kps, (int)tm, (int)tn};
       }
     }
   }
   return best;
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int S>
 hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int GM = 8;
@@ -442,7 +479,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     q.C = scratch;
     q.ldc = p.N;
     dim3 grid(pl.tiles_m * pl.tiles_n, pl.splits);
-    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
+    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
     int64_t g = (p.M * cols + 255) / 256;
     if (g > 4096) g = 4096;
@@ -455,12 +492,17 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     return hipGetLastError();
   }
   dim3 grid(pl.tiles_m * pl.tiles_n);
-  if (epi == EPI_SILU_BF16)
-    gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
-  else if (epi == EPI_BF16)
-    gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+  if constexpr ((BN / WGN / 32) % 2 == 0) {
+    if (epi == EPI_SILU_BF16) {
+      gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      return hipGetLastError();
+    }
+  }
+  if (epi == EPI_SILU_BF16) return hipErrorInvalidValue;   // the planner never picks such a variant
+  if (epi == EPI_BF16)
+    gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   else
-    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, false, GM><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   return hipGetLastError();
 }
 
@@ -504,11 +546,15 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const bool can_split = scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
   const Plan pl = make_plan(p.M, p.N, p.K, epi, can_split);
-  switch (pl.tile) {
-    case TILE_256x256: return launch_tile<256, 256, 4, 2>(p, epi, pl, scratch, s);
-    case TILE_128x128: return launch_tile<128, 128, 2, 2>(p, epi, pl, scratch, s);
-    case TILE_64x128: return launch_tile<64, 128, 2, 2>(p, epi, pl, scratch, s);
-    default: return launch_tile<128, 64, 4, 1>(p, epi, pl, scratch, s);
+  switch (pl.v) {
+    case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, epi, pl, scratch, s);
+    case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, epi, pl, scratch, s);
+    case V128x128_4: return launch_tile<128, 128, 2, 2, 4>(p, epi, pl, scratch, s);
+    case V128x128_2: return launch_tile<128, 128, 2, 2, 2>(p, epi, pl, scratch, s);
+    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, epi, pl, scratch, s);
+    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s);
+    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s);
+    default: return launch_tile<64, 64, 2, 2, 8>(p, epi, pl, scratch, s);
   }
 }
 
