@@ -1,241 +1,504 @@
 // Prefill attention over the rank's local heads ("Tensor parallelism from
 // scratch", "Implementation", TPAttention.forward): causal GQA attention of
-// T new tokens after `past` cached ones, query t (position past + t) sees
-// keys 0 .. past + t; q head i reads kv head i / rep; scale 1/sqrt(128).
+// T new tokens after `past` cached ones; query t (position past + t) sees
+// keys 0 .. past + t, q head i reads kv head i / rep, scale 1/sqrt(128).
 //
-// Flash-style on MFMA (v_mfma_f32_32x32x16_bf16).  A workgroup is 4 waves;
-// each wave owns 32 query rows of one q head, and the waves of a workgroup
-// share one kv head (up to 4 heads of the GQA group x the same rows, or
-// fewer heads x more rows), so every K/V tile staged in LDS serves 128
-// query rows.  Per 64-key tile:
-//   S^T[64 keys, 32 q] = K_tile . Q^T   (A = K rows from LDS, B = Q in VGPRs)
-// puts one query per lane column, so row max / row sum are lane-local plus
-// one exchange with lane ^ 32; then
-//   O^T[128 d, 32 q] += V^T . P^T       (A = V^T from LDS, B = P in VGPRs)
-// V is transposed while being written to LDS (4 keys x 8 d per thread).
-// The softmax runs in the exp2 domain with the running max per query.
+// Flash attention on MFMA (v_mfma_f32_32x32x16_bf16).  A workgroup is four
+// waves working on one kv head:
+//  * each wave owns 32 query rows of HW q heads of that kv head (HW = 2 under
+//    GQA, else 1), so every K or V operand it reads from LDS feeds HW MFMAs;
+//  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads
+//    with the lds flag) through a ring of NS stages; 16-byte chunks of a key
+//    row are XOR-swizzled by the key so that operand reads avoid bank
+//    conflicts;
+//  * S^T[64 keys, 32 q] = K . Q^T with Q^T held in VGPRs: each lane column
+//    is one query, so its row max and sum are lane-local plus one exchange
+//    with the other half-wave;
+//  * O^T[128 d, 32 q] += V^T . P^T, V^T read with the transposing LDS load
+//    ds_read_b64_tr_b16: in each 16-lane group, source lane s reads 4 d of
+//    key base + s/4 and lane i receives d = dbase + i of keys base .. base+3;
+//  * the softmax runs in the exp2 domain with a running max per query.
+// Early query blocks need few keys.  When the blocks alone cannot fill the
+// GPU, each block's key range is cut into chunks of `chunk` tiles; every
+// chunk leaves a partial (unnormalised O, max, sum) that a second kernel
+// merges in chunk order.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tps {
 
 namespace {
 
-constexpr int kTileKeys = 64;
-constexpr int kStage = kTileKeys * 128 * 2;   // bf16 elements: K tile + V^T tile
+typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+constexpr int kKeys = 64;                    // keys per tile
+constexpr int kTile = kKeys * 256;           // bytes of one K or V tile (64 rows x 128 bf16)
+constexpr int kStage = 2 * kTile;            // K tile, then V tile
+constexpr int kLoadsPerWave = kStage / 1024 / 4;
+constexpr float kQScale = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
+constexpr float kSlack = 8.f;                 // lazy-rescale margin, log2 units
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+// byte offset of 16-byte chunk c (d = 8c .. 8c+7) of key row `key` in a tile
+__device__ __forceinline__ uint32_t toff(int key, int c) { return (uint32_t)(key * 256 + ((c ^ (key & 15)) << 4)); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Workgroup barrier without the release fence of __syncthreads(), which
+// would wait for every outstanding direct-to-LDS load; each wave waits for
+// its own loads of the next tile (vmcnt) before arriving.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// K tile: [64 keys][16 chunks of 8 d]; chunk slot XOR (key & 15)
-__device__ __forceinline__ int k_off(int key, int chunk) { return key * 128 + ((chunk ^ (key & 15)) << 3); }
-// V^T tile: [128 d][16 granules of 4 keys]; granule slot XOR ((d >> 1) & 15)
-__device__ __forceinline__ int vt_off(int d, int granule) { return d * 64 + ((granule ^ ((d >> 1) & 15)) << 2); }
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// raw buffer descriptor: base, stride 0, num_records bytes (reads at or past
+// the end return zero)
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes land at LDS byte lds + 16 l.
+// Issued from asm so that the compiler, which would otherwise order every
+// later LDS read of the ring behind all outstanding loads (vmcnt(0)), leaves
+// the ordering to the explicit waits of the ring; M0 is set right here and
+// nothing else in these kernels reads it.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 
-template <int REP>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a, int n_tb, float qscale) {
-  constexpr int HPW = REP < 4 ? REP : 4;   // q heads per workgroup
-  constexpr int RB = 4 / HPW;              // 32-row blocks per workgroup
-  constexpr int ROWS = 32 * RB;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * kStage];
+struct PrefillPlan {
+  int rows;       // query rows per workgroup (32 per wave row block)
+  int n_rb;       // query row blocks
+  int hgroups;    // workgroups per kv head along the q heads
+  int chunk;      // key tiles per work item; 0: a block's whole key range
+  int items;      // work items per (batch, kv head, head group)
+};
 
-  // grid: [(b, kvh, head group) x row blocks]; heavy (late) row blocks first
-  const int tb = n_tb - 1 - (int)(blockIdx.x % n_tb);
-  int rest = blockIdx.x / n_tb;
-  const int hgroups = REP / HPW;
-  const int hg = rest % hgroups;
-  rest /= hgroups;
-  const int kvh = rest % a.lkv, b = rest / a.lkv;
+__host__ __device__ inline int rb_tiles(int T, int past, int rows, int r) {
+  const int end = (r + 1) * rows < T ? (r + 1) * rows : T;
+  return (past + end + kKeys - 1) / kKeys;
+}
+__host__ __device__ inline int rb_chunks(int T, int past, const PrefillPlan& p, int r) {
+  return p.chunk == 0 ? 1 : (rb_tiles(T, past, p.rows, r) + p.chunk - 1) / p.chunk;
+}
+// work items of a (batch, kv head, head group) run heaviest block first:
+// block n_rb - 1 chunks 0 .. , then block n_rb - 2, ...
+__device__ inline int item_base(int T, int past, const PrefillPlan& p, int r) {
+  int acc = 0;
+  for (int rr = p.n_rb - 1; rr > r; --rr) acc += rb_chunks(T, past, p, rr);
+  return acc;
+}
+
+template <int HW, int HG, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
+  constexpr int RB = 4 / HG;           // 32-row blocks per workgroup
+  constexpr int WGH = HW * HG;         // q heads per workgroup
+  // one array per ring stage: reads of one stage then carry alias scopes
+  // that tell them apart from direct-to-LDS loads still landing in another,
+  // so the compiler adds no wait for those loads before them
+  __shared__ __attribute__((aligned(16))) unsigned char smem0[kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char smem1[kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char smem2[NS > 2 ? kStage : 16];
+  static_assert(NS == 2 || NS == 3, "ring of two or three stages");
+  auto stage = [&](auto st) -> unsigned char* {
+    constexpr int v = decltype(st)::value;
+    return v == 0 ? smem0 : (v == 1 ? smem1 : smem2);
+  };
+
+  const int groups = a.B * a.lkv * p.hgroups;
+  const int w = blockIdx.x / groups, grp = blockIdx.x % groups;
+  const int hgrp = grp % p.hgroups;
+  const int kvh = (grp / p.hgroups) % a.lkv;
+  const int b = grp / (p.hgroups * a.lkv);
+  int r = p.n_rb - 1 - w, c = 0;
+  if (p.chunk != 0) {
+    int acc = 0;
+    for (r = p.n_rb - 1; r > 0; --r) {
+      const int ch = rb_chunks(a.T, a.past, p, r);
+      if (w < acc + ch) break;
+      acc += ch;
+    }
+    c = w - acc;
+  }
+  const int nt = rb_tiles(a.T, a.past, p.rows, r);
+  const int kt0 = p.chunk != 0 ? c * p.chunk : 0;
+  const int kt1 = p.chunk != 0 ? min(nt, kt0 + p.chunk) : nt;
+  const bool split = p.chunk != 0 && rb_chunks(a.T, a.past, p, r) > 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
-  const int hh = wave / RB, rr = wave % RB;
-  const int head = kvh * REP + hg * HPW + hh;
-  const int t0 = tb * ROWS;
-  const int tq = t0 + rr * 32 + lr;            // this lane's query row
-  const int qpos = a.past + tq;
+  const int hg = wave / RB, rr = wave % RB;
+  const int rep = a.lq / a.lkv;
+  const int head0 = kvh * rep + hgrp * WGH + hg * HW;
+  const int t0w = r * p.rows + rr * 32;                  // first query row of this wave
+  const bool active = t0w < a.T;
+  const int nt_w = active ? (a.past + min(a.T, t0w + 32) + kKeys - 1) / kKeys : 0;
+  const int qpos = a.past + t0w + lr;                    // this lane's query position
   const int64_t ldq = (int64_t)a.lq * 128;
 
-  // Q^T fragments: lane supplies q[tq, head, ks*16 + lh*8 .. +8]
-  bf16x8 qf[8];
+  // Q^T operands: lane supplies q[t0w + lr, head, ks*16 + lh*8 .. +8]
+  bf16x8 qf[HW][8];
   {
+    const int tq = t0w + lr;
     const bool ok = tq < a.T;
-    const bf16* qp = a.q + ((int64_t)b * a.T + (ok ? tq : 0)) * ldq + (int64_t)head * 128 + lh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 r = ok ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = *reinterpret_cast<bf16x8*>(&r);
-    }
-  }
-
-  const int t_end = min(a.T, t0 + ROWS);                 // rows of this block
-  const int n_keys = a.past + t_end;                     // keys any row needs
-  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int64_t slab = ((int64_t)b * a.lkv + kvh) * a.S_max * 128;
-  const bf16* kg = a.k_cache + slab;
-  const bf16* vg = a.v_cache + slab;
-
-  // tile loaders: K 4 chunks per thread; V 4 keys x 8 d per thread
-  u32x4 kr[4], vr[4];
-  const int vq = tid >> 4, vdc = tid & 15;              // key quad, d chunk
-  auto gload = [&](int tile) {
-    const int key0 = tile * kTileKeys;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + i * 256, key = q >> 4, c = q & 15;
-      kr[i] = key0 + key < n_keys ? *reinterpret_cast<const u32x4*>(kg + (int64_t)(key0 + key) * 128 + c * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + vq * 4 + i;
-      vr[i] = key < n_keys ? *reinterpret_cast<const u32x4*>(vg + (int64_t)key * 128 + vdc * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-    bf16* sk = smem + buf * kStage;
-    bf16* sv = sk + kTileKeys * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + i * 256, key = q >> 4, c = q & 15;
-      *reinterpret_cast<u32x4*>(sk + k_off(key, c)) = kr[i];
-    }
-    // transpose: for d = vdc*8 + j, the 4 keys vq*4 .. +3 form one granule
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = j >> 1;
-      uint32_t lo, hi;
-      if (j & 1) {
-        lo = (vr[0][w] >> 16) | (vr[1][w] & 0xFFFF0000u);
-        hi = (vr[2][w] >> 16) | (vr[3][w] & 0xFFFF0000u);
-      } else {
-        lo = (vr[0][w] & 0xFFFFu) | (vr[1][w] << 16);
-        hi = (vr[2][w] & 0xFFFFu) | (vr[3][w] << 16);
-      }
-      *reinterpret_cast<u32x2*>(sv + vt_off(vdc * 8 + j, vq)) = u32x2{lo, hi};
-    }
-  };
-
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int cur = tile & 1;
-    if (tile + 1 < n_tiles) gload(tile + 1);
-    const bf16* sk = smem + cur * kStage;
-    const bf16* sv = sk + kTileKeys * 128;
-
-    // S^T for keys kb*32 .. +32
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+    for (int hw = 0; hw < HW; ++hw) {
+      const bf16* qp = a.q + ((int64_t)b * a.T + (ok ? tq : 0)) * ldq + (int64_t)(head0 + hw) * 128 + lh * 8;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int key = kb * 32 + lr;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + k_off(key, ks * 2 + lh));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+        qf[hw][ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    // scale, causal mask, running max
-    const int key0 = tile * kTileKeys;
-    float mt = -INFINITY;
+    // land Q before the ring starts: a first use inside the loop would make
+    // the compiler wait for every load in flight on each iteration
+    wait_vm<0>();
+  }
+
+  // K/V loads: load i (0..15) of a tile holds keys 4i .. 4i+3; lane l writes
+  // physical chunk l % 16 of key 4i + l / 16.  Keys at or past past + T read
+  // as zero (descriptor bound) and are masked as lying after every query.
+  const int64_t slab = ((int64_t)b * a.lkv + kvh) * a.S_max * 128;
+  const uint32_t valid_bytes = (uint32_t)(a.past + a.T) * 256u;
+  const i32x4 rk = buffer_rsrc(a.k_cache + slab, valid_bytes);
+  const i32x4 rv = buffer_rsrc(a.v_cache + slab, valid_bytes);
+  auto dma_tile = [&](int kt, auto st) {
+    const uint32_t base = lds_addr(stage(st));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < 4; ++j) {
+      const int i = wave * 4 + j;
+      const int key = 4 * i + (lane >> 4);
+      const uint32_t off = (uint32_t)(kt * kKeys + key) * 256u + (uint32_t)(((lane & 15) ^ (key & 15)) << 4);
+      dma16(rk, off, base + i * 1024);
+      dma16(rv, off, base + kTile + i * 1024);
+    }
+  };
+
+  f32x16 o[HW][4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-        const float v = key <= qpos ? s[kb][e] * qscale : -INFINITY;
-        s[kb][e] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m_run, mt);
-    const float corr = m_run == -INFINITY ? 0.f : ex2(m_run - mn);
-    m_run = mn;
-    float ps = 0.f;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = s[kb][e] == -INFINITY ? 0.f : ex2(s[kb][e] - mn);
-        ps += p;
-        pf[kb * 2 + (e >> 3)][e & 7] = f2bf(p);
-      }
-    l_run = l_run * corr + ps;
+  for (int hw = 0; hw < HW; ++hw)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= corr;
-    // O^T += V^T P^T; k-step ks covers keys (ks/2)*32 + (ks%2)*16 .. +16
+      for (int e = 0; e < 16; ++e) o[hw][db][e] = 0.f;
+  float m_run[HW], l_run[HW];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int g0 = ((ks >> 1) * 32 + (ks & 1) * 16) / 4 + lh;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + lr;
-        const u32x2 x = *reinterpret_cast<const u32x2*>(sv + vt_off(d, g0));
-        const u32x2 y = *reinterpret_cast<const u32x2*>(sv + vt_off(d, g0 + 2));
-        u32x4 r = {x[0], x[1], y[0], y[1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<bf16x8*>(&r), pf[ks], o[db], 0, 0, 0);
-      }
-    }
-    if (tile + 1 < n_tiles) sstore(cur ^ 1);
-    __syncthreads();
+  for (int hw = 0; hw < HW; ++hw) {
+    m_run[hw] = -INFINITY;
+    l_run[hw] = 0.f;
   }
 
-  // normalise; stage [32 q][128 d] per wave through LDS for 16-byte stores
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  bf16* so = smem + wave * (32 * 128);
+  // transposing-read source address of this lane for V^T rows db*32 ..,
+  // keys kbase .. kbase+3 of its half-wave (lanes 16g .. 16g+15, g = lane/16)
+  const int trg = lane >> 4, tri = lane & 15;
+  const int tr_key = 4 * (trg >> 1) + (tri >> 2);          // + kb*32 + sub*16 + rd*8
+  const int tr_d = (trg & 1) * 16 + 4 * (tri & 3);         // + db*32
+  auto compute = [&](int kt, auto st) {
+    const unsigned char* K = stage(st);
+    const unsigned char* V = K + kTile;
+    f32x16 s[HW][2];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int hw = 0; hw < HW; ++hw)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int d = db * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-      so[lr * 128 + (((d >> 3) ^ (lr & 15)) << 3) + (d & 7)] = f2bf(o[db][e] * inv);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[hw][kb][e] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + toff(kb * 32 + lr, ks * 2 + lh));
+#pragma unroll
+        for (int hw = 0; hw < HW; ++hw)
+          s[hw][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[hw][ks], s[hw][kb], 0, 0, 0);
+      }
+    const int key0 = kt * kKeys;
+    const bool diag = key0 + kKeys - 1 > a.past + t0w;     // some key may follow some row
+    bf16x8 pf[HW][4];
+#pragma unroll
+    for (int hw = 0; hw < HW; ++hw) {
+      // raw max over this tile's visible scores (the scale is positive)
+      float mx = -INFINITY;
+      if (diag) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (key0 + kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3) > qpos) s[hw][kb][e] = -INFINITY;
+            mx = fmaxf(mx, s[hw][kb][e]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hw][kb][e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kQScale;
+      // Lazy rescale: the exponent base m_run only moves when some row's max
+      // passes it by more than kSlack, so P stays below 2^kSlack and O and
+      // l, which share the base, stay exact; most tiles skip the O update.
+      if (__any(mx > m_run[hw] + kSlack)) {
+        const float mn = fmaxf(m_run[hw], mx);
+        const float corr = m_run[hw] == -INFINITY ? 0.f : ex2(m_run[hw] - mn);
+        m_run[hw] = mn;
+        l_run[hw] *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[hw][db][e] *= corr;
+      }
+      const float base = m_run[hw] == -INFINITY ? 0.f : m_run[hw];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = ex2(__builtin_fmaf(s[hw][kb][e], kQScale, -base));   // masked: 2^-inf = 0
+          ps += pv;
+          pf[hw][kb * 2 + (e >> 3)][e & 7] = f2bf(pv);
+        }
+      l_run[hw] += ps;
     }
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = lane + i * 64, row = q >> 4, c = q & 15;
-    const int t = t0 + rr * 32 + row;
-    if (t < a.T) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(so + row * 128 + ((c ^ (row & 15)) << 3));
-      *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.T + t) * ldq + (int64_t)head * 128 + c * 8) = v;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int key = kb * 32 + sub * 16 + tr_key;
+          const int d = db * 32 + tr_d;
+          const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
+          const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+          const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
+          const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
+          const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int hw = 0; hw < HW; ++hw)
+            o[hw][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hw][kb * 2 + sub], o[hw][db], 0, 0, 0);
+        }
+  };
+
+  // ring: tiles kt0 + i live in stage i % NS; NS - 1 tiles in flight.  The
+  // loop is unrolled by NS so that every stage index is a constant.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, (NS > 2 ? 2 : 0)>;
+  const int ntiles = kt1 - kt0;
+  dma_tile(kt0, S0{});
+  if (NS > 2 && ntiles > 1) dma_tile(kt0 + 1, S1{});
+  if (NS > 2 && ntiles > 1)
+    wait_vm<(NS - 2) * kLoadsPerWave>();
+  else
+    wait_vm<0>();
+  barrier();
+  // one ring step: tile i in stage `cur`, tile i + NS - 1 goes to `nxt`
+  auto step = [&](int i, auto cur, auto nxt) {
+    const bool issue = i + NS - 1 < ntiles;
+    if (issue) dma_tile(kt0 + i + NS - 1, nxt);
+    const int kt = kt0 + i;
+    if (kt < nt_w) compute(kt, cur);
+    if (i + 1 < ntiles) {
+      if (issue)
+        wait_vm<(NS - 2) * kLoadsPerWave>();
+      else
+        wait_vm<0>();
+      barrier();
     }
+  };
+  for (int i = 0; i < ntiles; i += NS) {
+    if constexpr (NS == 3) {
+      step(i, S0{}, S2{});
+      if (i + 1 < ntiles) step(i + 1, S1{}, S0{});
+      if (i + 2 < ntiles) step(i + 2, S2{}, S1{});
+    } else {
+      step(i, S0{}, S1{});
+      if (i + 1 < ntiles) step(i + 1, S1{}, S0{});
+    }
+  }
+
+  // 8 KB staging region ri of the (wave, head) outputs: stage ri / 4
+  auto stage_region = [&](int ri) -> bf16* {
+    unsigned char* base = ri < 4 ? smem0 : smem1;
+    return reinterpret_cast<bf16*>(base + (ri & 3) * (32 * 128 * 2));
+  };
+  if (!split) {
+    // normalise; stage [32 q][128 d] per (wave, head) through LDS, then
+    // write whole 16-byte chunks of each row
+    __syncthreads();   // the staging area overlaps the ring
+#pragma unroll
+    for (int hw = 0; hw < HW; ++hw) {
+      const float l = l_run[hw] + __shfl_xor(l_run[hw], 32, 64);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16* so = stage_region(wave * HW + hw);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int d = db * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+          so[lr * 128 + (((d >> 3) ^ (lr & 15)) << 3) + (d & 7)] = f2bf(o[hw][db][e] * inv);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    if (!active) return;
+#pragma unroll
+    for (int hw = 0; hw < HW; ++hw) {
+      const bf16* so = stage_region(wave * HW + hw);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = lane + i * 64, row = q >> 4, cc = q & 15;
+        const int t = t0w + row;
+        if (t < a.T) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(so + row * 128 + ((cc ^ (row & 15)) << 3));
+          *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.T + t) * ldq + (int64_t)(head0 + hw) * 128 + cc * 8) = v;
+        }
+      }
+    }
+    return;
+  }
+  // split: unnormalised O and (max, sum) per row for the merge kernel
+  if (!active) return;
+  const int64_t item = (int64_t)grp * p.items + w;
+  const int64_t n_items = (int64_t)groups * p.items;
+  float* po = a.scratch;
+  float2* pml = reinterpret_cast<float2*>(a.scratch + n_items * WGH * p.rows * 128);
+#pragma unroll
+  for (int hw = 0; hw < HW; ++hw) {
+    const int wh = hg * HW + hw;
+    const int row = rr * 32 + lr;
+    float* dst = po + ((item * WGH + wh) * p.rows + row) * 128;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = db * 32 + 8 * e4 + 4 * lh;
+        *reinterpret_cast<f32x4*>(dst + d) =
+            f32x4{o[hw][db][e4 * 4], o[hw][db][e4 * 4 + 1], o[hw][db][e4 * 4 + 2], o[hw][db][e4 * 4 + 3]};
+      }
+    const float l = l_run[hw] + __shfl_xor(l_run[hw], 32, 64);
+    if (lh == 0) pml[(item * WGH + wh) * p.rows + row] = float2{m_run[hw], l};
   }
 }
 
-template <int REP>
-hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  constexpr int HPW = REP < 4 ? REP : 4;
-  constexpr int ROWS = 32 * (4 / HPW);
-  const int n_tb = (a.T + ROWS - 1) / ROWS;
-  const int64_t blocks = (int64_t)n_tb * (REP / HPW) * a.lkv * a.B;
-  const float qscale = 0.08838834764831845f * 1.4426950408889634f;   // log2(e)/sqrt(128)
-  attn_prefill_kernel<REP><<<(unsigned)blocks, 256, 0, s>>>(a, n_tb, qscale);
+// Merges the chunk partials of split row blocks, one thread per (row, head,
+// 4 d): O = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i with m = max_i m_i,
+// summed in chunk order.
+template <int WGH>
+__global__ __launch_bounds__(256) void attn_prefill_merge(AttnArgs a, PrefillPlan p) {
+  const int groups = a.B * a.lkv * p.hgroups;
+  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int dc = (int)(gid & 31);
+  gid >>= 5;
+  const int row = (int)(gid % p.rows);
+  gid /= p.rows;
+  const int wh = (int)(gid % WGH);
+  gid /= WGH;
+  const int grp = (int)(gid % groups);
+  const int r = (int)(gid / groups);
+  if (r >= p.n_rb) return;
+  const int t = r * p.rows + row;
+  const int n = rb_chunks(a.T, a.past, p, r);
+  if (n <= 1 || t >= a.T) return;
+  const int hgrp = grp % p.hgroups;
+  const int kvh = (grp / p.hgroups) % a.lkv;
+  const int b = grp / (p.hgroups * a.lkv);
+  const int64_t first = (int64_t)grp * p.items + item_base(a.T, a.past, p, r);
+  const int64_t n_items = (int64_t)groups * p.items;
+  const float* po = a.scratch;
+  const float2* pml = reinterpret_cast<const float2*>(a.scratch + n_items * WGH * p.rows * 128);
+  float m = -INFINITY;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, pml[((first + i) * WGH + wh) * p.rows + row].x);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < n; ++i) {
+    const float2 ml = pml[((first + i) * WGH + wh) * p.rows + row];
+    const float wgt = ml.x == -INFINITY ? 0.f : ex2(ml.x - m);
+    l += wgt * ml.y;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(po + (((first + i) * WGH + wh) * p.rows + row) * 128 + dc * 4);
+    acc += wgt * v;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const bf16x4 ob = {f2bf(acc[0] * inv), f2bf(acc[1] * inv), f2bf(acc[2] * inv), f2bf(acc[3] * inv)};
+  const int head = kvh * (a.lq / a.lkv) + hgrp * WGH + wh;
+  *reinterpret_cast<bf16x4*>(a.out + ((int64_t)b * a.T + t) * a.lq * 128 + (int64_t)head * 128 + dc * 4) = ob;
+}
+
+constexpr int kStages = 3;
+
+// q heads per wave and waves along the heads for a GQA ratio
+void prefill_shape(int rep, int* hw, int* hg) {
+  *hw = rep >= 2 ? 2 : 1;
+  const int g = rep / *hw;
+  *hg = g < 4 ? g : 4;
+}
+
+PrefillPlan prefill_plan(int B, int T, int past, int lq, int lkv) {
+  int hw, hg;
+  prefill_shape(lq / lkv, &hw, &hg);
+  PrefillPlan p{};
+  p.rows = 32 * (4 / hg);
+  p.n_rb = (T + p.rows - 1) / p.rows;
+  p.hgroups = lq / lkv / (hw * hg);
+  p.chunk = 0;
+  p.items = p.n_rb;
+  const int64_t groups = (int64_t)B * lkv * p.hgroups;
+  if (groups * p.n_rb >= 256) return p;
+  // cut key ranges so that about one work item per CU exists, each of at
+  // least two tiles
+  int64_t total = 0;
+  for (int r = 0; r < p.n_rb; ++r) total += rb_tiles(T, past, p.rows, r);
+  total *= groups;
+  int chunk = (int)((total + 255) / 256);
+  if (chunk < 2) chunk = 2;
+  PrefillPlan q = p;
+  q.chunk = chunk;
+  q.items = 0;
+  for (int r = 0; r < p.n_rb; ++r) q.items += rb_chunks(T, past, q, r);
+  return q.items > p.n_rb ? q : p;
+}
+
+template <int HW, int HG>
+hipError_t launch(const AttnArgs& a, const PrefillPlan& p, hipStream_t s) {
+  const int64_t groups = (int64_t)a.B * a.lkv * p.hgroups;
+  attn_prefill_kernel<HW, HG, kStages><<<(unsigned)(groups * p.items), 256, 0, s>>>(a, p);
+  if (p.chunk != 0) {
+    const int64_t threads = groups * p.n_rb * (HW * HG) * p.rows * 32;
+    attn_prefill_merge<HW * HG><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a, p);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t attn_prefill_scratch_bytes(int B, int T, int past, int lq, int lkv) {
+  if (B <= 0 || T <= 0 || lkv <= 0) return 0;
+  const PrefillPlan p = prefill_plan(B, T, past, lq, lkv);
+  if (p.chunk == 0) return 0;
+  int hw, hg;
+  prefill_shape(lq / lkv, &hw, &hg);
+  const int64_t items = (int64_t)B * lkv * p.hgroups * p.items;
+  return (size_t)items * hw * hg * p.rows * (128 + 2) * sizeof(float);
+}
+
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
+  const PrefillPlan p = prefill_plan(a.B, a.T, a.past, a.lq, a.lkv);
+  if (p.chunk != 0 && a.scratch == nullptr) return hipErrorInvalidValue;
   switch (a.lq / a.lkv) {
-    case 1: return launch<1>(a, s);
-    case 2: return launch<2>(a, s);
-    case 4: return launch<4>(a, s);
-    case 8: return launch<8>(a, s);
-    case 16: return launch<16>(a, s);
+    case 1: return launch<1, 1>(a, p, s);
+    case 2: return launch<2, 1>(a, p, s);
+    case 4: return launch<2, 2>(a, p, s);
+    case 8: return launch<2, 4>(a, p, s);
+    case 16: return launch<2, 4>(a, p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -76,10 +76,11 @@ struct AttnArgs {
   const bf16* k_cache;   // [B, lkv, S_max, 128]
   const bf16* v_cache;
   bf16* out;             // [B*T, lq*128]
-  float* scratch;        // decode split partials
+  float* scratch;        // split partials (decode: KV splits; prefill: key chunks)
   int B, T, past, S_max, lq, lkv;
 };
 size_t attn_decode_scratch_bytes(int B, int lq, int lkv, int ctx);
+size_t attn_prefill_scratch_bytes(int B, int T, int past, int lq, int lkv);
 hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 

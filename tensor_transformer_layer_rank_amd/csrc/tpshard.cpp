@@ -74,6 +74,9 @@ AttnWs attn_ws(const tp_cfg* c, const tp_local& L, int64_t B, int64_t T, int64_t
   if (T == 1 && B > 0) {
     const size_t sd = attn_decode_scratch_bytes((int)B, L.lq, L.lkv, (int)(past + 1));
     if (sd > sb) sb = sd;
+  } else if (T > 1 && B > 0) {
+    const size_t sp = attn_prefill_scratch_bytes((int)B, (int)T, (int)past, L.lq, L.lkv);
+    if (sp > sb) sb = sp;
   }
   w.scratch_bytes = align_up(sb);
   w.total = w.scratch + w.scratch_bytes;
