@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 ARCH = "gfx950"
 
-SOURCES = ["tpshard.cpp", "copy_kernels.hip", "gemm.hip", "qkv_epilogue.hip", "attn_decode.hip",
+SOURCES = ["tpshard.cpp", "copy_kernels.hip", "gemm.hip", "attn_decode.hip",
            "attn_prefill.hip"]
 
 

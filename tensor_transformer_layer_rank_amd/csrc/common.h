@@ -24,9 +24,25 @@ __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // RNE (v_cv
 // C[M, N] = A[M, K] * B[N, K]^T, A and B bf16 with K contiguous, fp32
 // accumulation.  Epilogues:
 enum GemmEpi {
-  EPI_BF16 = 0,      // C bf16 [M, N] (row stride ldc)
-  EPI_F32 = 1,       // C fp32 [M, N]; with split-K: partials [splits, M, N]
-  EPI_SILU_BF16 = 2  // B = [gate; up] with `li` rows each; C = silu(gate)*up, bf16 [M, li]
+  EPI_BF16 = 0,       // C bf16 [M, N] (row stride ldc)
+  EPI_F32 = 1,        // C fp32 [M, N]; with split-K: partials [splits, M, N]
+  EPI_SILU_BF16 = 2,  // B = [gate; up] with `li` rows each; C = silu(gate)*up, bf16 [M, li]
+  EPI_QKV = 3         // merged q/k/v projection finished per head (QkvArgs); C unused
+};
+
+// Per-head finish of the merged QKV projection (row m = b*T + t, N = (lq +
+// 2 lkv) * 128 columns, head h = column / 128): q and k heads get the QK-norm
+// v / sqrt(mean(v^2) + eps) * w and the rotate-half RoPE at position past + t;
+// q heads go to q_out [M, lq*128], k and v heads to the caches
+// [B, lkv, S_max, 128] at position past + t.
+struct QkvArgs {
+  const bf16* q_norm_w;  // [128]
+  const bf16* k_norm_w;  // [128]
+  bf16* q_out;
+  bf16* k_cache;
+  bf16* v_cache;
+  int B, T, past, S_max, lq, lkv;
+  float eps, theta;
 };
 
 struct GemmProblem {
@@ -36,6 +52,7 @@ struct GemmProblem {
   int64_t M, N, K;      // N = rows of B (for EPI_SILU_BF16: 2*li)
   int64_t lda, ldb, ldc;
   int64_t li;           // EPI_SILU_BF16 only
+  QkvArgs qkv;          // EPI_QKV only
 };
 
 // Chooses a tile shape and launches.  When the grid would not fill the GPU
@@ -59,17 +76,6 @@ hipError_t embed_masked(const int32_t* ids, int64_t n, const void* table, int64_
                         int64_t vend, int64_t H, int esize, void* out, hipStream_t s);
 
 // --- attention block ------------------------------------------------------
-struct QkvArgs {
-  const float* qkv;      // [M, n_qkv] fp32 projection output
-  const bf16* q_norm_w;  // [128]
-  const bf16* k_norm_w;  // [128]
-  bf16* q_out;           // [M, lq*128]
-  bf16* k_cache;         // [B, lkv, S_max, 128]
-  bf16* v_cache;
-  int B, T, past, S_max, lq, lkv;
-  float eps, theta;
-};
-hipError_t qkv_norm_rope_store(const QkvArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const bf16* q;         // [B*T, lq*128]

@@ -56,6 +56,67 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+// ---- merged QKV finish ("Tensor parallelism from scratch", "Implementation",
+// TPAttention.forward: QK-norm per head, RoPE at the absolute position, cache
+// append).  Norm: v / sqrt(mean(v^2) + eps) * w; RoPE: rotate-half, the pair
+// (v[i], v[i+64]) turns by pos * theta^(-2i/128) (Qwen3 conventions, which
+// the pages import without printing).
+//
+// 16 lanes hold one (row, head): lane j has d = 8j .. 8j+7, so the pair
+// partner of lane j is lane j ^ 8 and the norm is a 16-lane reduction.
+// rope_coef() gives theta^(-2i/128) / (2 pi) for the lane's 8 indices i; the
+// angle in revolutions is reduced in double (positions reach ~1e6) before the
+// fp32 sine and cosine.
+__device__ __forceinline__ void rope_coef(float theta, int j, double (&cr)[8]) {
+  const double l2t = log2((double)theta);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = (8 * j + e) & 63;
+    cr[e] = exp2(-(double)(2 * i) / 128.0 * l2t) * 0.159154943091895335768883;
+  }
+}
+__device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
+                                           const double (&cr)[8]) {
+  const int b = (int)(m / a.T), t = (int)(m - (int64_t)b * a.T);
+  const int pos = a.past + t;
+  if (h < a.lq + a.lkv) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    ss += __shfl_xor(ss, 8, 64);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>((h < a.lq ? a.q_norm_w : a.k_norm_w) + 8 * j);
+    const bf16x8 w = __builtin_bit_cast(bf16x8, wv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= inv * bf2f(w[e]);
+    float xp[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xp[e] = __shfl_xor(x[e], 8, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double rev = (double)pos * cr[e];
+      rev -= rint(rev);
+      const float ang = (float)(rev * 6.283185307179586476925);
+      const float sn = __sinf(ang), cs = __cosf(ang);
+      x[e] = j < 8 ? x[e] * cs - xp[e] * sn : x[e] * cs + xp[e] * sn;
+    }
+  }
+  bf16* dst;
+  if (h < a.lq)
+    dst = a.q_out + m * ((int64_t)a.lq * 128) + (int64_t)h * 128;
+  else if (h < a.lq + a.lkv)
+    dst = a.k_cache + (((int64_t)b * a.lkv + (h - a.lq)) * a.S_max + pos) * 128;
+  else
+    dst = a.v_cache + (((int64_t)b * a.lkv + (h - a.lq - a.lkv)) * a.S_max + pos) * 128;
+  const bf16x8 o = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3]), f2bf(x[4]), f2bf(x[5]), f2bf(x[6]), f2bf(x[7])};
+  *reinterpret_cast<bf16x8*>(dst + 8 * j) = o;
+}
+// the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
+constexpr bool qkv_tile_ok(int bm, int bn, int stages) { return bn % 128 == 0 && bm * bn * 4 <= stages * (bm + bn) * 128; }
+
 // Default LDS stages per tile shape: as many as let two workgroups share a
 // CU's 160 KB (at least 2, at most 6).  Weight-streaming shapes (few rows)
 // pick deeper rings explicitly.
@@ -299,6 +360,39 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 
   // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
   // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block.
+  if constexpr (EPI == EPI_QKV) {
+    static_assert(qkv_tile_ok(BM, BN, S), "QKV tile must cover whole heads and fit the ring");
+    // stage the fp32 tile [BM][BN] in LDS (16-byte chunk c of row r at
+    // c ^ ((r >> 2) & 1): the two half-waves write rows 4 apart), then
+    // finish it 16 lanes per (row, head)
+    __syncthreads();
+    float* st = reinterpret_cast<float*>(smem);
+    auto st_off = [&](int r, int c) -> int { return r * BN + ((((c >> 2) ^ (r >> 2)) & 1) | ((c >> 2) & ~1)) * 4 + (c & 3); };
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          st[st_off(wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), ncol(j) + lr)] = acc[i][j][e];
+    __syncthreads();
+    const int j16 = tid & 15;
+    double cr[8];
+    rope_coef(p.qkv.theta, j16, cr);
+    constexpr int HPT = BN / 128;                      // heads per tile
+    const int heads = (int)(p.N / 128);
+    for (int u = tid >> 4; u < BM * HPT; u += NT / 16) {
+      const int r = u % BM, hh = u / BM;
+      const int64_t m = m0 + r;
+      const int h = tn * HPT + hh;
+      if (m >= M || h >= heads) continue;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = st[st_off(r, hh * 128 + 8 * j16 + e)];
+      qkv_finish(p.qkv, x, m, h, j16, cr);
+    }
+    return;
+  }
   if (EPI == EPI_F32) {
     float* C = static_cast<float*>(p.C) + (SPLIT ? (int64_t)blockIdx.y * M * p.ldc : 0);
     const bool full = m0 + BM <= M && (int64_t)(tn + 1) * BN <= p.N;
@@ -393,6 +487,32 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
   }
 }
 
+// Sums the split-K partials of a merged QKV projection in split order and
+// finishes each (row, head), 16 lanes per unit.
+__global__ __launch_bounds__(256) void splitk_reduce_qkv(const float* __restrict__ part, int splits, int64_t M,
+                                                         int64_t N, QkvArgs a) {
+  const int heads = (int)(N / 128);
+  const int j = threadIdx.x & 15;
+  double cr[8];
+  rope_coef(a.theta, j, cr);
+  for (int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; u < M * heads; u += (int64_t)gridDim.x * 16) {
+    const int64_t m = u / heads;
+    const int h = (int)(u - m * heads);
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) {
+      const float* src = part + ((int64_t)z * M + m) * N + (int64_t)h * 128 + 8 * j;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] += v0[e];
+        x[4 + e] += v1[e];
+      }
+    }
+    qkv_finish(a, x, m, h, j, cr);
+  }
+}
+
 // ---- tile-shape choice -----------------------------------------------------
 //
 // Each variant is a tile shape, a wave layout and an LDS ring depth.  The
@@ -457,6 +577,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split) {
     for (int64_t sp = 1; sp <= 8; ++sp) {
       if (sp > 1 && (!allow_split || kblocks < 8 * sp)) break;
       if (epi == EPI_SILU_BF16 && sp == 1 && !v.silu) continue;
+      if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
       const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn) * (sp > 1 ? 1.05 : 1.0);
@@ -483,7 +604,11 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
     int64_t g = (p.M * cols + 255) / 256;
     if (g > 4096) g = 4096;
-    if (epi == EPI_SILU_BF16)
+    if (epi == EPI_QKV) {
+      int64_t gq = (p.M * (p.N / 128) * 16 + 255) / 256;
+      if (gq > 4096) gq = 4096;
+      splitk_reduce_qkv<<<(int)gq, 256, 0, s>>>((const float*)scratch, pl.splits, p.M, p.N, p.qkv);
+    } else if (epi == EPI_SILU_BF16)
       splitk_reduce<EPI_SILU_BF16><<<(int)g, 256, 0, s>>>((const float*)scratch, pl.splits, p.M, p.N, p.C, p.ldc, p.li);
     else if (epi == EPI_BF16)
       splitk_reduce<EPI_BF16><<<(int)g, 256, 0, s>>>((const float*)scratch, pl.splits, p.M, p.N, p.C, p.ldc, 0);
@@ -498,7 +623,14 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
       return hipGetLastError();
     }
   }
-  if (epi == EPI_SILU_BF16) return hipErrorInvalidValue;   // the planner never picks such a variant
+  if constexpr (qkv_tile_ok(BM, BN, S)) {
+    if (epi == EPI_QKV) {
+      gemm_kernel<BM, BN, WGM, WGN, EPI_QKV, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      return hipGetLastError();
+    }
+  }
+  // the planner never picks a variant that cannot run the epilogue
+  if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
   if (epi == EPI_BF16)
     gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   else

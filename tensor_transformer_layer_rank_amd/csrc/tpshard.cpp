@@ -59,16 +59,15 @@ int esize_of(const tp_cfg* c) { return c->dtype == TP_BF16 ? 2 : 4; }
 
 // workspace layout of tp_qkv_attn (each region 256-byte aligned)
 struct AttnWs {
-  size_t qkv, q, attn, scratch, scratch_bytes, total;
+  size_t q, attn, scratch, scratch_bytes, total;
 };
 AttnWs attn_ws(const tp_cfg* c, const tp_local& L, int64_t B, int64_t T, int64_t past) {
   const int64_t M = B * T;
   AttnWs w{};
-  w.qkv = 0;
-  w.q = w.qkv + align_up((size_t)(M * L.n_qkv) * 4);
+  w.q = 0;
   w.attn = w.q + align_up((size_t)(M * L.lq * 128) * 2);
   w.scratch = w.attn + align_up((size_t)(M * L.lq * 128) * 2);
-  size_t sb = gemm_scratch_bytes(M, L.n_qkv, c->hidden, EPI_F32);
+  size_t sb = gemm_scratch_bytes(M, L.n_qkv, c->hidden, EPI_QKV);
   const size_t so = gemm_scratch_bytes(M, c->hidden, (int64_t)L.lq * 128, EPI_BF16);
   if (so > sb) sb = so;
   if (T == 1 && B > 0) {
@@ -237,27 +236,24 @@ int tp_qkv_attn(const tp_cfg* cfg, const void* x, int32_t B, int32_t T, int32_t 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const int64_t M = (int64_t)B * T, H = cfg->hidden, lqd = (int64_t)L.lq * 128;
-  float* qkv = reinterpret_cast<float*>(ws + w.qkv);
   bf16* q = q_out_opt ? static_cast<bf16*>(q_out_opt) : reinterpret_cast<bf16*>(ws + w.q);
   bf16* attn = attn_out_opt ? static_cast<bf16*>(attn_out_opt) : reinterpret_cast<bf16*>(ws + w.attn);
   void* scratch = ws + w.scratch;
 
-  // 1. merged column-parallel projection (fp32 result)
-  GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(w_qkv), qkv, M, L.n_qkv, H, H, H, L.n_qkv, 0};
-  hipError_t e = gemm_bf16(g, EPI_F32, scratch, w.scratch_bytes, s);
+  // 1. merged column-parallel projection, finished per head in the epilogue:
+  //    QK-norm, RoPE, q to its buffer, k and v appended to the caches
+  GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(w_qkv), nullptr, M, L.n_qkv, H, H, H, 0, 0};
+  g.qkv = QkvArgs{static_cast<const bf16*>(q_norm_w), static_cast<const bf16*>(k_norm_w), q,
+                  static_cast<bf16*>(k_cache), static_cast<bf16*>(v_cache), B, T, past_len, S_max, L.lq, L.lkv,
+                  cfg->rms_eps, cfg->rope_theta};
+  hipError_t e = gemm_bf16(g, EPI_QKV, scratch, w.scratch_bytes, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
-  // 2. QK-norm, RoPE, cache append
-  QkvArgs qa{qkv, static_cast<const bf16*>(q_norm_w), static_cast<const bf16*>(k_norm_w), q,
-             static_cast<bf16*>(k_cache), static_cast<bf16*>(v_cache), B, T, past_len, S_max, L.lq, L.lkv,
-             cfg->rms_eps, cfg->rope_theta};
-  e = qkv_norm_rope_store(qa, s);
-  if (e != hipSuccess) return TP_ERR_LAUNCH;
-  // 3. attention over the local heads
+  // 2. attention over the local heads
   AttnArgs aa{q, static_cast<const bf16*>(k_cache), static_cast<const bf16*>(v_cache), attn,
               reinterpret_cast<float*>(scratch), B, T, past_len, S_max, L.lq, L.lkv};
   e = T == 1 ? attn_decode(aa, s) : attn_prefill(aa, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
-  // 4. row-parallel o_proj -> partial sum
+  // 3. row-parallel o_proj -> partial sum
   GemmProblem go{attn, static_cast<const bf16*>(w_o), out_partial, M, H, lqd, lqd, lqd, H, 0};
   return launched(gemm_bf16(go, EPI_BF16, scratch, w.scratch_bytes, s));
 }
