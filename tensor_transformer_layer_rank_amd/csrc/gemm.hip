@@ -170,43 +170,45 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 
   // Tile loads.  Wave w fills 8-row groups g = w, w + NW, ... of each
   // stage; lane l of a group writes LDS row 8g + l/8, physical chunk l%8,
-  // and so fetches the logical chunk that the swizzle puts there.  Sources
-  // are buffer descriptors over the tile's rows of A and B, advanced by k0
-  // per block; rows past the matrix fall outside the descriptor (they only
-  // feed outputs that are never stored).
+  // and so fetches the logical chunk that the swizzle puts there.  One
+  // buffer descriptor per operand covers the tile's rows from column 0 to
+  // the end of the matrix; a block at column k0 adds 2*k0 to the lane
+  // offsets, so the range check drops exactly what lies past the matrix
+  // (rows past M or N, and columns past the last row's end).  Those zeros
+  // only feed outputs that are never stored, or are cleared by zero_tail.
   constexpr int NW = WGM * WGN;
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "8-row groups must split evenly");
   static_assert(EPI != EPI_SILU_BF16 || (BN / 2) % 8 == 0, "gate/up halves must hold whole groups");
   constexpr int A_G = BM / (8 * NW), B_G = BN / (8 * NW);
+  constexpr int NV = A_G + B_G;             // direct-to-LDS loads per block per wave
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int grow = lane >> 3, gpc = lane & 7;
   const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
   // B rows of this tile: [b_row0, +BN) or, for silu, [gate0, +BN/2) and [up0, +BN/2)
   const int64_t nrow0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) : (int64_t)tn * BN;
   const int64_t nrows = EPI == EPI_SILU_BF16 ? p.li - nrow0 : p.N - nrow0;
-  const bf16* a_base = p.A + m0 * p.lda;
-  const bf16* b_base = p.B + nrow0 * p.ldb;
-  const bf16* u_base = p.B + (p.li + nrow0) * p.ldb;   // silu only
-  // lane offset inside a group's 8 rows (bytes), with the swizzled chunk
-  auto goff = [&](int row, int64_t ld_b) -> uint32_t {
-    return (uint32_t)(row * ld_b + ((gpc ^ ((row >> 1) & 7)) << 4));
-  };
-  // one whole K block into LDS stage `buf` (prologue)
-  auto dma_block = [&](int64_t k0, int buf) {
-    bf16* sA = smem + buf * STAGE;
-    bf16* sB = sA + BM * BK;
-    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(a_base + k0, (M - m0) * lda_b - k0 * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.B + (p.li + nrow0) * p.ldb, nrows * ldb_b);   // silu only
+  // per-slice lane offsets (bytes, column 0) and LDS destinations within a stage
+  uint32_t voff[NV];
 #pragma unroll
-    for (int i = 0; i < A_G; ++i) {
-      const int g = wave + i * NW;
-      dma16(ra_, goff(g * 8 + grow, lda_b), sA + g * 8 * BK);
-    }
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(b_base + k0, nrows * ldb_b - k0 * 2);
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(u_base + k0, nrows * ldb_b - k0 * 2);
-#pragma unroll
-    for (int i = 0; i < B_G; ++i) {
-      const int g = wave + i * NW;
+  for (int v = 0; v < NV; ++v) {
+    const bool isA = v < A_G;
+    const int g = wave + (isA ? v : v - A_G) * NW;
+    const bool up = !isA && EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
+    const int row = g * 8 + grow - (up ? BN / 2 : 0);
+    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + ((gpc ^ ((row >> 1) & 7)) << 4));
+  }
+  auto dma_slice = [&](int v, int64_t k0, int buf) {
+    bf16* st = smem + buf * STAGE;
+    const uint32_t ko = (uint32_t)(k0 * 2);
+    if (v < A_G) {
+      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * 8 * BK);
+    } else {
+      const int g = wave_u + (v - A_G) * NW;
       const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-      dma16(up ? ru : rg, goff(g * 8 + grow - (up ? BN / 2 : 0), ldb_b), sB + g * 8 * BK);
+      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * 8 * BK);
     }
   };
   // The last block may end inside the 64-wide K window: its columns at or
@@ -236,127 +238,135 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 
   const int lr = lane & 31, lh = lane >> 5;
   bf16x8 af[2][TM], bfr[2][TN];
-  // One K block from LDS stage `cur`, written in issue order and fenced so
-  // the compiler keeps it: per k-step, MFMAs go out two at a time, each pair
-  // followed by one operand read for the next k-step and, every other pair,
-  // one slice of the next block's direct-to-LDS loads.  LDS latency and the
-  // texture path then overlap the matrix pipe instead of taking turns.
+  // One K block is KS k-steps of 16.  Each k-step's MFMAs go out two at a
+  // time in a fenced, hand-ordered stream (sched_barrier keeps it): after
+  // each pair come the operand reads of the following k-step and, in the
+  // first k-step, slices of a later block's direct-to-LDS loads.  In the
+  // last k-step the wave waits for the next block (vmcnt, then a barrier)
+  // after half of its MFMAs, and reads the next block's first operands
+  // under the other half, so a block boundary leaves no gap in the matrix
+  // pipe.  Fragment set ks & 1 holds k-step ks (KS is even).
   constexpr int KS = BK / 16;
-  constexpr int NF = TM + TN, NMF = TM * TN, NV = A_G + B_G;
+  static_assert(KS % 2 == 0, "fragment sets alternate per k-step");
+  constexpr int NF = TM + TN, NMF = TM * TN;
   constexpr int NPAIR = (NMF + 1) / 2;
   constexpr int RDP = (NF + NPAIR - 1) / NPAIR;   // operand reads after each MFMA pair
-  auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int buf, int x) {
+  constexpr int H1 = NPAIR / 2;                    // pairs of the last k-step before the wait
+  constexpr int RDP2 = (NF + (NPAIR - H1) - 1) / (NPAIR - H1);
+  auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int fs, int x) {
     // order A0, B0..B(TN-1), A1..A(TM-1): the next k-step's first MFMAs
     // need A0 with every B
     const int c = ks * 2 + lh;
     if (x == 0 || x > TN) {
       const int i = x == 0 ? 0 : x - TN;
       const int row = wm * WM + i * 32 + lr;
-      af[buf][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
+      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
     } else {
       const int row = ncol(x - 1) + lr;
-      bfr[buf][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
+      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
     }
   };
-  // dma_tag: std::true_type when this iteration issues a later block's
-  // loads (compile-time, so the fenced stream has no branches)
-  auto compute = [&](auto dma_tag, int cur, int64_t next_k0, int next_buf) {
-    constexpr bool dma = decltype(dma_tag)::value;
-    const bf16* sA = smem + cur * STAGE;
-    const bf16* sB = sA + BM * BK;
-    bf16* nA = smem + next_buf * STAGE;
-    bf16* nB = nA + BM * BK;
-    __amdgpu_buffer_rsrc_t ra_, rg, ru;
-    if constexpr (dma) {
-      ra_ = make_rsrc(a_base + next_k0, (M - m0) * lda_b - next_k0 * 2);
-      rg = make_rsrc(b_base + next_k0, nrows * ldb_b - next_k0 * 2);
-      ru = make_rsrc(u_base + next_k0, nrows * ldb_b - next_k0 * 2);
-    }
-    auto dma_slice = [&](int v) {
-      if (v < A_G) {
-        const int g = wave + v * NW;
-        dma16(ra_, goff(g * 8 + grow, lda_b), nA + g * 8 * BK);
-      } else {
-        const int g = wave + (v - A_G) * NW;
-        const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-        dma16(up ? ru : rg, goff(g * 8 + grow - (up ? BN / 2 : 0), ldb_b), nB + g * 8 * BK);
-      }
-    };
-    __builtin_amdgcn_sched_barrier(0);
+  auto mfma_pair = [&](int fs, int pr) {
 #pragma unroll
-    for (int x = 0; x < NF; ++x) read_frag(sA, sB, 0, 0, x);
-    __builtin_amdgcn_sched_barrier(0);
-    int v = 0;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int pr = 0; pr < NPAIR; ++pr) {
-#pragma unroll
-        for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m)
-          acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][m / TN], bfr[ks & 1][m % TN],
-                                                                      acc[m / TN][m % TN], 0, 0, 0);
-        if (ks + 1 < KS) {
-#pragma unroll
-          for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
-        }
-        // spread the NV loads evenly over the KS * NPAIR pairs
-        if constexpr (dma) {
-          if (v < NV && (ks * NPAIR + pr + 1) * NV >= (v + 1) * KS * NPAIR) dma_slice(v++);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if constexpr (dma) {
-      while (v < NV) dma_slice(v++);
-    }
+    for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m)
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
+                                                                  acc[m / TN][m % TN], 0, 0, 0);
   };
-
-  // Pipeline: blocks 0 .. S-2 are issued up front; iteration kt computes
-  // stage kt % S while the loads of block kt + S - 1 go out between its
-  // MFMAs, then waits until block kt + 1 has landed (vmcnt counts this
-  // wave's outstanding loads, which complete in issue order).
-  constexpr int NVW = A_G + B_G;            // loads per block per wave
   const bool tail = (kend - kbeg) % BK != 0;
   auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
   // A bare s_barrier, not __syncthreads(): the latter's workgroup release
   // fence waits for every outstanding direct-to-LDS load (vmcnt(0)), which
-  // would collapse the ring to one block in flight.  The wait_vm<> before
-  // each settle already guarantees that this wave's loads of the next block
-  // have landed; the barrier makes that true for all waves.  The asm memory
-  // clobber keeps the compiler from moving LDS accesses across it.
+  // would collapse the ring to one block in flight.  Before it each wave
+  // has waited (vmcnt) for its own loads of the block about to be read and
+  // (lgkmcnt) for its reads of the block just finished; the barrier makes
+  // both true for all waves, so the block can be read and the stage it
+  // frees can be refilled.  The asm memory clobber keeps the compiler from
+  // moving LDS accesses across it.
   auto settle = [&](int blk) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
     if (tail && blk == nk - 1) {
       zero_tail(blk % S, kblk(blk));
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zero stores are done
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // the zero stores are done
       asm volatile("s_barrier" ::: "memory");
     }
   };
+  // One block from stage kt % S.  DMA: this block issues block kt + S - 1
+  // (steady state); NEXT: a block kt + 1 follows; SD: the steady-state
+  // wait (S - 2 blocks may stay in flight) rather than vmcnt(0).
+  auto block = [&](auto dma_tag, auto next_tag, int kt) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const int cur = kt % S;
+    const bf16* sA = smem + cur * STAGE;
+    const bf16* sB = sA + BM * BK;
+    const int nxt = (kt + 1) % S;
+    const bf16* nA = smem + nxt * STAGE;
+    const bf16* nB = nA + BM * BK;
+    const int64_t dk0 = kblk(kt + S - 1);
+    const int dbuf = (kt + S - 1) % S;
+    __builtin_amdgcn_sched_barrier(0);
+    int v = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+      for (int pr = 0; pr < NPAIR; ++pr) {
+        mfma_pair(ks & 1, pr);
+#pragma unroll
+        for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
+        if constexpr (DMA) {
+          if (ks == 0) {
+            while (v < NV && (pr + 1) * NV >= (v + 1) * NPAIR) dma_slice(v++, dk0, dbuf);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int pr = 0; pr < H1; ++pr) {
+      mfma_pair(1, pr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) {
+      if constexpr (DMA)
+        wait_vm<(S - 2) * NV>();
+      else
+        wait_vm0();
+      settle(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int pr = H1; pr < NPAIR; ++pr) {
+      mfma_pair(1, pr);
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int x = (pr - H1) * RDP2; x < (pr - H1) * RDP2 + RDP2 && x < NF; ++x) read_frag(nA, nB, 0, 0, x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Pipeline: blocks 0 .. S-2 are issued up front; block kt issues block
+  // kt + S - 1 in its first k-step and waits for block kt + 1 in its last
+  // (vmcnt counts this wave's outstanding loads, which complete in issue
+  // order).
   if (nk > 0) {
     const int pro = nk < S - 1 ? nk : S - 1;
-    for (int blk = 0; blk < pro; ++blk) dma_block(kblk(blk), blk);
+    for (int blk = 0; blk < pro; ++blk)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) dma_slice(v, kblk(blk), blk);
     if (pro - 1 == S - 2)
-      wait_vm<(S - 2) * NVW>();
+      wait_vm<(S - 2) * NV>();
     else
       wait_vm0();
     settle(0);
+#pragma unroll
+    for (int x = 0; x < NF; ++x) read_frag(smem, smem + BM * BK, 0, 0, x);
   }
-  // steady state: every iteration issues block kt + S - 1 and has exactly
-  // S - 2 blocks in flight behind block kt + 1
   int kt = 0;
-  for (; kt + S - 1 < nk; ++kt) {
-    compute(std::true_type{}, kt % S, kblk(kt + S - 1), (kt + S - 1) % S);
-    wait_vm<(S - 2) * NVW>();
-    settle(kt + 1);
-  }
-  // drain: nothing left to issue
-  for (; kt < nk; ++kt) {
-    compute(std::false_type{}, kt % S, 0, 0);
-    if (kt + 1 < nk) {
-      wait_vm0();
-      settle(kt + 1);
-    }
-  }
+  for (; kt + S - 1 < nk; ++kt) block(std::true_type{}, std::true_type{}, kt);      // steady state
+  for (; kt + 1 < nk; ++kt) block(std::false_type{}, std::true_type{}, kt);         // drain
+  if (kt < nk) block(std::false_type{}, std::false_type{}, kt);                     // last block
 
   // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
   // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block.
@@ -452,7 +462,10 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     if (gm >= M || gc >= ncols) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * OC + ((c ^ (r & (OCH - 1))) << 3));
     if (vec && gc + 8 <= ncols) {
-      *reinterpret_cast<u32x4*>(C + gm * p.ldc + gc) = v;
+      // streaming store: the output is not read again by this kernel, and
+      // allocating it in L2 would evict the A/B panels that other tiles
+      // still read (the lm_head writes four times the bytes it reads)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + gm * p.ldc + gc));
     } else {
       const bf16* e = reinterpret_cast<const bf16*>(&v);
       for (int t = 0; t < 8 && gc + t < ncols; ++t) C[gm * p.ldc + gc + t] = e[t];
