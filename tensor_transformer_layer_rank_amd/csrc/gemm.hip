@@ -467,10 +467,337 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       // still read (the lm_head writes four times the bytes it reads)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + gm * p.ldc + gc));
     } else {
-      const bf16* e = reinterpret_cast<const bf16*>(&v);
-      for (int t = 0; t < 8 && gc + t < ncols; ++t) C[gm * p.ldc + gc + t] = e[t];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (gc + t < ncols) C[gm * p.ldc + gc + t] = __builtin_bit_cast(bf16, (uint16_t)(v[t >> 1] >> (16 * (t & 1))));
     }
   }
+}
+
+// Persistent variant for grids of many tiles (bf16 and silu epilogues): one
+// workgroup per CU walks a share of the tiles of its XCD, and the LDS ring
+// runs on across tile boundaries, so the next tile's first block is already
+// in LDS (and its first operands in VGPRs) when a tile ends, and no
+// workgroup launch, pipeline fill or ring drain separates two tiles.  The
+// epilogue stages each wave's outputs, 32 rows x 64 columns at a time,
+// through a 4 KB LDS region of its own next to the ring, so it needs no
+// workgroup barrier and never touches a ring stage.
+//
+// Tile order: the tiles (GROUP_M-grouped as in gemm_kernel) are cut into 8
+// contiguous ranges, one per XCD; workgroup b runs on XCD b % 8 (the
+// dispatcher deals workgroups round-robin) and takes every G-th tile of its
+// XCD's range, G = the XCD's workgroup count, so the CUs of one XCD work on
+// neighbouring tiles at any time and share A and B panels in its L2.
+template <int BM, int BN, int WGM, int WGN, int EPI, int GROUP_M, int S>
+__global__ __launch_bounds__(WGM * WGN * 64)
+__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_SILU_BF16, "bf16 outputs only");
+  constexpr int BK = 64;
+  constexpr int NW = WGM * WGN, NT = NW * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int KC = BK / 8;
+  constexpr int STAGE = (BM + BN) * BK;
+  constexpr int RING = S * STAGE * 2;               // bytes
+  constexpr int OCW = EPI == EPI_SILU_BF16 ? WN / 2 : WN;   // output columns per wave
+  static_assert(OCW % 64 == 0 && TN % 2 == 0, "epilogue passes are 32 x 64");
+  static_assert(RING + NW * 4096 <= 163840, "ring and staging must fit the CU's LDS");
+  __shared__ __attribute__((aligned(16))) bf16 smem[(RING + NW * 4096) / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int64_t M = p.M, K = p.K;
+  const int nk = (int)((K + BK - 1) / BK);
+  const bool tail = K % BK != 0;
+
+  // this workgroup's tiles: first + j * step, j < n_my
+  int first, step, n_my;
+  {
+    const int ntiles = tiles_m * tiles_n;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int per = ntiles / kXcds, rem = ntiles % kXcds;
+    const int cs = xcd * per + min(xcd, rem), len = per + (xcd < rem);
+    const int g = ((int)gridDim.x - xcd + kXcds - 1) / kXcds;
+    first = cs + slot;
+    step = g;
+    n_my = slot < len ? (len - slot + g - 1) / g : 0;
+  }
+  auto coords = [&](int j, int64_t& m0, int64_t& nrow0) __attribute__((always_inline)) {
+    const int t = first + j * step;
+    const int per_group = GROUP_M * tiles_n;
+    const int gi = t / per_group;
+    const int first_m = gi * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int r = t - gi * per_group;
+    m0 = (int64_t)(first_m + r % gm) * BM;
+    nrow0 = (int64_t)(r / gm) * (EPI == EPI_SILU_BF16 ? BN / 2 : BN);
+  };
+
+  constexpr int A_G = BM / (8 * NW), B_G = BN / (8 * NW), NV = A_G + B_G;
+  const int grow = lane >> 3, gpc = lane & 7;
+  const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
+  uint32_t voff[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const bool isA = v < A_G;
+    const int g = wave + (isA ? v : v - A_G) * NW;
+    const bool up = !isA && EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
+    const int row = g * 8 + grow - (up ? BN / 2 : 0);
+    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + ((gpc ^ ((row >> 1) & 7)) << 4));
+  }
+  // descriptors of the tile that the loads are filling (they run ahead of
+  // the MFMAs by S - 1 blocks, so into the next tile near a tile's end)
+  __amdgpu_buffer_rsrc_t ra, rg, ru;
+  auto set_dma_tile = [&](int j) __attribute__((always_inline)) {
+    int64_t m0, nrow0;
+    coords(j, m0, nrow0);
+    const int64_t nrows = EPI == EPI_SILU_BF16 ? p.li - nrow0 : p.N - nrow0;
+    ra = make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
+    rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
+    ru = make_rsrc(p.B + (p.li + nrow0) * p.ldb, nrows * ldb_b);
+  };
+  int dj = 0, dkb = 0;                    // tile and K block of the next load
+  auto dma_next = [&](int buf) __attribute__((always_inline)) {
+    if (dkb == 0) set_dma_tile(dj);
+    bf16* st = smem + buf * STAGE;
+    const uint32_t ko = (uint32_t)dkb * (BK * 2);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if (v < A_G) {
+        dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * 8 * BK);
+      } else {
+        const int g = wave_u + (v - A_G) * NW;
+        const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
+        dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * 8 * BK);
+      }
+    }
+    if (++dkb == nk) {
+      dkb = 0;
+      ++dj;
+    }
+  };
+  // one slice of the next load (issued inside the fenced MFMA stream)
+  auto dma_slice = [&](int v, int buf) __attribute__((always_inline)) {
+    bf16* st = smem + buf * STAGE;
+    const uint32_t ko = (uint32_t)dkb * (BK * 2);
+    if (v < A_G) {
+      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * 8 * BK);
+    } else {
+      const int g = wave_u + (v - A_G) * NW;
+      const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
+      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * 8 * BK);
+    }
+  };
+  auto zero_tail = [&](int buf) __attribute__((always_inline)) {
+    bf16* st = smem + buf * STAGE;
+    const int64_t k0 = (int64_t)(nk - 1) * BK;
+    for (int q = tid; q < (BM + BN) * KC; q += NT) {
+      const int row = q / KC, lc = q % KC;
+      if (k0 + lc * 8 >= K) *reinterpret_cast<u32x4*>(st + row * BK + swz(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto ncol = [&](int j) __attribute__((always_inline)) -> int {
+    if (EPI == EPI_SILU_BF16)
+      return j < TN / 2 ? wn * (WN / 2) + j * 32 : BN / 2 + wn * (WN / 2) + (j - TN / 2) * 32;
+    return wn * WN + j * 32;
+  };
+
+  f32x16 acc[TM][TN];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  };
+  zero_acc();
+  bf16x8 af[2][TM], bfr[2][TN];
+  constexpr int KS = BK / 16;
+  constexpr int NF = TM + TN, NMF = TM * TN;
+  constexpr int NPAIR = (NMF + 1) / 2;
+  constexpr int RDP = (NF + NPAIR - 1) / NPAIR;
+  constexpr int H1 = NPAIR / 2;
+  constexpr int RDP2 = (NF + (NPAIR - H1) - 1) / (NPAIR - H1);
+  auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int fs, int x) __attribute__((always_inline)) {
+    const int c = ks * 2 + lh;
+    if (x == 0 || x > TN) {
+      const int i = x == 0 ? 0 : x - TN;
+      const int row = wm * WM + i * 32 + lr;
+      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
+    } else {
+      const int row = ncol(x - 1) + lr;
+      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
+    }
+  };
+  auto mfma_pair = [&](int fs, int pr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m)
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
+                                                                  acc[m / TN][m % TN], 0, 0, 0);
+  };
+  // the block just landed in `buf` is read next: all waves have their
+  // loads of it (vmcnt, before the call) and are done reading the stage it
+  // frees (lgkmcnt); a tile's last block also has its K tail cleared
+  auto settle = [&](int buf, bool last_of_tile) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+    if (tail && last_of_tile) {
+      zero_tail(buf);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      asm volatile("s_barrier" ::: "memory");
+    }
+  };
+
+  // epilogue of tile j through this wave's staging region
+  bf16* so = smem + RING / 2 + wave_u * 2048;
+  auto epilogue = [&](int j) __attribute__((always_inline)) {
+    int64_t m0, nrow0;
+    coords(j, m0, nrow0);
+    const int64_t ncols = EPI == EPI_SILU_BF16 ? p.li : p.N;
+    const int64_t col0 = nrow0 + wn * OCW;       // output column of this wave's first column
+    bf16* C = static_cast<bf16*>(p.C);
+    const bool vec = (p.ldc % 8) == 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int ps = 0; ps < OCW / 64; ++ps) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 8 * (e >> 2) + 4 * lh + (e & 3), c = jj * 32 + lr;
+            float v;
+            if (EPI == EPI_SILU_BF16) {
+              const float g = acc[i][ps * 2 + jj][e], u = acc[i][ps * 2 + jj + TN / 2][e];
+              v = g / (1.f + __expf(-g)) * u;
+            } else {
+              v = acc[i][ps * 2 + jj][e];
+            }
+            so[r * 64 + (((c >> 3) ^ (r & 7)) << 3) + (c & 7)] = f2bf(v);
+          }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = lane + 64 * u, r = q >> 3, cc = q & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * 64 + ((cc ^ (r & 7)) << 3));
+          const int64_t gm = m0 + wm * WM + i * 32 + r, gc = col0 + ps * 64 + cc * 8;
+          if (gm < M && gc < ncols) {
+            if (vec && gc + 8 <= ncols) {
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + gm * p.ldc + gc));
+            } else {
+#pragma unroll
+              for (int t = 0; t < 8; ++t)
+                if (gc + t < ncols)
+                  C[gm * p.ldc + gc + t] = __builtin_bit_cast(bf16, (uint16_t)(v[t >> 1] >> (16 * (t & 1))));
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next pass overwrites
+        __builtin_amdgcn_wave_barrier();
+      }
+  };
+
+  const int total = n_my * nk;
+  int ckb = 0, cj = 0;                    // K block and tile of the block being computed
+  // block gb: stage gb % S; it issues block gb + S - 1 (DMA) and, unless it
+  // is the last one, waits for block gb + 1 and reads its first operands
+  auto block = [&](auto dma_tag, auto next_tag, int gb) __attribute__((always_inline)) {
+    constexpr bool DMA = decltype(dma_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const int cur = gb % S;
+    const bf16* sA = smem + cur * STAGE;
+    const bf16* sB = sA + BM * BK;
+    const int nxt = (gb + 1) % S;
+    const bf16* nA = smem + nxt * STAGE;
+    const bf16* nB = nA + BM * BK;
+    const int dbuf = (gb + S - 1) % S;
+    if constexpr (DMA) {
+      if (dkb == 0) set_dma_tile(dj);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int v = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+      for (int pr = 0; pr < NPAIR; ++pr) {
+        mfma_pair(ks & 1, pr);
+#pragma unroll
+        for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
+        if constexpr (DMA) {
+          if (ks == 0) {
+            while (v < NV && (pr + 1) * NV >= (v + 1) * NPAIR) dma_slice(v++, dbuf);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (DMA) {
+      if (++dkb == nk) {
+        dkb = 0;
+        ++dj;
+      }
+    }
+#pragma unroll
+    for (int pr = 0; pr < H1; ++pr) {
+      mfma_pair(1, pr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) {
+      if constexpr (DMA)
+        wait_vm<(S - 2) * NV>();
+      else
+        wait_vm0();
+      settle(nxt, nk == 1 || ckb + 1 == nk - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // at a tile's end the next operands are read after the epilogue, which
+    // then has the registers of the fragment set to itself
+    const bool tile_end = ckb == nk - 1;
+#pragma unroll
+    for (int pr = H1; pr < NPAIR; ++pr) {
+      mfma_pair(1, pr);
+      if constexpr (NEXT) {
+        if (!tile_end) {
+#pragma unroll
+          for (int x = (pr - H1) * RDP2; x < (pr - H1) * RDP2 + RDP2 && x < NF; ++x) read_frag(nA, nB, 0, 0, x);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tile_end) {
+      epilogue(cj);
+      zero_acc();
+      ckb = 0;
+      ++cj;
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int x = 0; x < NF; ++x) read_frag(nA, nB, 0, 0, x);
+      }
+    } else {
+      ++ckb;
+    }
+  };
+
+  if (total > 0) {
+    const int pro = total < S - 1 ? total : S - 1;
+    for (int blk = 0; blk < pro; ++blk) dma_next(blk);
+    if (pro - 1 == S - 2)
+      wait_vm<(S - 2) * NV>();
+    else
+      wait_vm0();
+    settle(0, nk == 1);
+#pragma unroll
+    for (int x = 0; x < NF; ++x) read_frag(smem, smem + BM * BK, 0, 0, x);
+  }
+  int gb = 0;
+  for (; gb + S - 1 < total; ++gb) block(std::true_type{}, std::true_type{}, gb);
+  for (; gb + 1 < total; ++gb) block(std::false_type{}, std::true_type{}, gb);
+  if (gb < total) block(std::false_type{}, std::false_type{}, gb);
 }
 
 // Sums split-K partials [splits, M, N] in a fixed order and applies the
@@ -691,6 +1018,13 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const bool can_split = scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
   const Plan pl = make_plan(p.M, p.N, p.K, epi, can_split);
+  // eight or more rounds of 256 x 256 tiles: one persistent workgroup per
+  // CU (measured: faster from about that many rounds on, when the per-tile
+  // fill and relaunch it saves are a visible part of a tile's time)
+  if (pl.v == V256x256 && pl.splits == 1 && epi == EPI_BF16 && (int64_t)pl.tiles_m * pl.tiles_n >= 8 * kCUs) {
+    gemm_persist_kernel<256, 256, 4, 2, EPI_BF16, 8, 2><<<kCUs, 512, 0, s>>>(p, pl.tiles_m, pl.tiles_n);
+    return hipGetLastError();
+  }
   switch (pl.v) {
     case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, epi, pl, scratch, s);
     case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, epi, pl, scratch, s);

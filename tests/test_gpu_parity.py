@@ -201,7 +201,7 @@ def test_embed_vocab_bit_exact_and_vocab_sum(case):
 
 # ------------------------------------------------------------------ lm_head
 
-@pytest.mark.parametrize("case", ["w3", "mid"])
+@pytest.mark.parametrize("case", ["w3", "mid", "many-ragged"])
 def test_lm_head(case):
     if case == "w3":
         w = synth.WORKLOADS[3]
@@ -210,6 +210,15 @@ def test_lm_head(case):
         x = synth.activations(3, M, H)
         rows = np.unique(np.concatenate([[0, 1, M - 1], np.random.default_rng(3).integers(0, M, 13)]))
         ranks = [0, 1]
+    elif case == "many-ragged":
+        # over eight rounds of 256 x 256 tiles (the persistent kernel), with
+        # ragged M, N and K tails
+        V, H, n, M = 116400, 1000, 2, 2100
+        E = synth.embedding(12, V, H)
+        x = synth.activations(12, M, H)
+        rows = np.unique(np.concatenate([[0, 255, 256, 1279, 1280, 2047, 2048, M - 1],
+                                         np.random.default_rng(12).integers(0, M, 8)]))
+        ranks = [1]
     else:
         V, H, n, M = 777, 520, 2, 300
         E = synth.embedding(11, V, H)
