@@ -21,8 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 ARCH = "gfx950"
 
-SOURCES = ["tpshard.cpp", "copy_kernels.hip", "gemm.hip", "attn_decode.hip",
-           "attn_prefill.hip"]
+SOURCES = ["tpshard.cpp", "copy_kernels.hip", "gemm.hip", "attn_prefill.hip",
+           "attn_flash.hip"]
 
 
 def hipcc() -> str:

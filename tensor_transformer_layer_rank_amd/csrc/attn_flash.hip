@@ -1,0 +1,292 @@
+// Attention over the rank's local heads, prefill and decode ("Tensor
+// parallelism from scratch", "Implementation", TPAttention.forward; "Two ways
+// to split": heads are independent, so a rank attends with its own q heads
+// over its own kv-cache heads; q head i reads kv head i / rep):
+//
+//   out[t, h, :] = sum_s softmax_s(q[t,h] . k[h/rep, s] / sqrt(128)) v[h/rep, s]
+//   over the keys s = 0 .. past + t (query t sits at position past + t).
+//
+// Flash attention on MFMA (v_mfma_f32_32x32x16_bf16).  A workgroup owns 32
+// query rows that share one kv head:
+//  * prefill: 32 consecutive tokens of one q head;
+//  * decode (T = 1): the rep q heads of one (sequence, kv head), one row
+//    each (rows past rep are padding and never stored).
+// Its four waves split the block's key range into four contiguous parts.
+// Each wave streams its part through a private ring of two LDS stages
+// (32-key K and V tiles, direct global->LDS buffer loads, 16-byte chunks of
+// a key row XOR-swizzled by the key so that operand reads avoid bank
+// conflicts) and keeps an online softmax in the exp2 domain:
+//  * S^T[32 keys, 32 q] = K . Q^T with Q^T in VGPRs: each lane column is one
+//    query row, so its max and sum are lane-local plus one exchange with the
+//    other half-wave;
+//  * O^T[128 d, 32 q] += V^T . P^T, V^T read with the transposing LDS load
+//    ds_read_b64_tr_b16.
+// The four partial (max, sum, O) are merged through LDS at the end, so a
+// block needs no second pass; prefill blocks run heaviest (latest) first.
+#include "common.h"
+
+namespace tps {
+
+namespace {
+
+typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKeys = 32;                    // keys per tile
+constexpr int kTileB = kKeys * 256;          // bytes of one K or V tile
+constexpr int kStageB = 2 * kTileB;          // K tile, then V tile
+constexpr int kWaveRingB = 2 * kStageB;      // two stages per wave
+constexpr int kLoads = kTileB / 1024;        // 1 KB direct-to-LDS loads per tile (K or V)
+constexpr int kMergeStride = 129;            // floats per merged row (odd: no bank conflicts)
+constexpr float kQScale = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
+constexpr float kSlack = 8.f;                 // lazy-rescale margin, log2 units
+static_assert(4 * 32 * (kMergeStride + 2) * 4 <= 4 * kWaveRingB, "merge area fits the rings");
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+// byte offset of 16-byte chunk c (d = 8c .. 8c+7) of key row `key` in a tile
+__device__ __forceinline__ uint32_t toff(int key, int c) { return (uint32_t)(key * 256 + ((c ^ (key & 15)) << 4)); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// raw buffer descriptor: base, stride 0, num_records bytes (reads at or past
+// the end return zero)
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes land at LDS byte lds + 16 l.
+// Issued from asm so that the compiler, which would otherwise order every
+// later LDS read behind all outstanding loads (vmcnt(0)), leaves the
+// ordering to the explicit waits of the ring; M0 is set right here and
+// nothing else in this kernel reads it.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_flash_kernel(AttnArgs a, int n_rb) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kWaveRingB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int rep = a.lq / a.lkv;
+  const bool decode = a.T == 1;
+  const int64_t ldq = (int64_t)a.lq * 128;
+
+  // the block: sequence b, kv head kvh, first q head head0, first token t0
+  int b, kvh, head0, t0;
+  if (decode) {
+    b = blockIdx.x / a.lkv;
+    kvh = blockIdx.x % a.lkv;
+    head0 = kvh * rep;
+    t0 = 0;
+  } else {
+    const int per_rb = a.B * a.lq;
+    const int rb = n_rb - 1 - (int)(blockIdx.x / per_rb);
+    const int rest = (int)(blockIdx.x % per_rb);
+    b = rest / a.lq;
+    head0 = rest % a.lq;
+    kvh = head0 / rep;
+    t0 = rb * 32;
+  }
+  const bool row_ok = decode ? lr < rep : t0 + lr < a.T;
+  const int qpos = a.past + (decode ? 0 : t0 + lr);       // this lane column's query position
+  const int min_pos = a.past + t0;                        // the block's first query position
+  const int n_keys = decode ? a.past + 1 : a.past + min(a.T, t0 + 32);
+  const int nt = (n_keys + kKeys - 1) / kKeys;
+  const int w0 = wave * nt / 4, w1 = (wave + 1) * nt / 4;   // this wave's tiles
+
+  // Q^T operands: lane supplies q[row lr, ks*16 + lh*8 .. +8]
+  bf16x8 qf[8];
+  {
+    const bf16* qp = decode ? a.q + (int64_t)b * ldq + (int64_t)(head0 + (row_ok ? lr : 0)) * 128
+                            : a.q + ((int64_t)b * a.T + (row_ok ? t0 + lr : 0)) * ldq + (int64_t)head0 * 128;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qp + ks * 16 + lh * 8) : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    // land Q before the ring starts: a first use inside the loop would make
+    // the compiler wait for every load in flight there
+    wait_vm<0>();
+  }
+
+  // K/V tile loads: load i (0..7) of a tile holds keys 4i .. 4i+3; lane l
+  // writes physical chunk l % 16 of key 4i + l / 16.  Keys at or past
+  // past + T read as zero (descriptor bound) and are masked.
+  const int64_t slab = ((int64_t)b * a.lkv + kvh) * a.S_max * 128;
+  const uint32_t valid_bytes = (uint32_t)(a.past + a.T) * 256u;
+  const i32x4 rk = buffer_rsrc(a.k_cache + slab, valid_bytes);
+  const i32x4 rv = buffer_rsrc(a.v_cache + slab, valid_bytes);
+  unsigned char* ring = smem + wave * kWaveRingB;
+  auto dma_tile = [&](int kt, int st) {
+    const uint32_t base = lds_addr(ring + st * kStageB);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int key = 4 * i + (lane >> 4);
+      const uint32_t off = (uint32_t)(kt * kKeys + key) * 256u + (uint32_t)(((lane & 15) ^ (key & 15)) << 4);
+      dma16(rk, off, base + i * 1024);
+      dma16(rv, off, base + kTileB + i * 1024);
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // transposing-read source address of this lane for V^T rows db*32 ..,
+  // keys kbase .. kbase+3 of its half-wave (lanes 16g .. 16g+15, g = lane/16)
+  const int trg = lane >> 4, tri = lane & 15;
+  const int tr_key = 4 * (trg >> 1) + (tri >> 2);          // + sub*16 + rd*8
+  const int tr_d = (trg & 1) * 16 + 4 * (tri & 3);         // + db*32
+  auto compute = [&](int kt, int st) {
+    const unsigned char* K = ring + st * kStageB;
+    const unsigned char* V = K + kTileB;
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + toff(lr, ks * 2 + lh));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+    const int key0 = kt * kKeys;
+    // raw max over this tile's visible scores (the scale is positive)
+    float mx = -INFINITY;
+    if (key0 + kKeys - 1 > min_pos) {                      // some key may follow some row
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (key0 + 8 * (e >> 2) + 4 * lh + (e & 3) > qpos) s[e] = -INFINITY;
+        mx = fmaxf(mx, s[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kQScale;
+    // Lazy rescale: the exponent base m_run only moves when some row's max
+    // passes it by more than kSlack, so P stays below 2^kSlack and O and l,
+    // which share the base, stay exact; most tiles skip the O update.
+    if (__any(mx > m_run + kSlack)) {
+      const float mn = fmaxf(m_run, mx);
+      const float corr = m_run == -INFINITY ? 0.f : ex2(m_run - mn);
+      m_run = mn;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= corr;
+    }
+    const float base = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pf[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = ex2(__builtin_fmaf(s[e], kQScale, -base));   // masked: 2^-inf = 0
+      ps += pv;
+      pf[e >> 3][e & 7] = f2bf(pv);
+    }
+    l_run += ps;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int key = sub * 16 + tr_key;
+        const int d = db * 32 + tr_d;
+        const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
+        const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+        const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
+        const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
+        const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sub], o[db], 0, 0, 0);
+      }
+  };
+
+  // this wave's ring: tile w0 + i lives in stage i % 2; the next tile's
+  // loads go out before the current one is computed.  The stage a load
+  // refills was read by the previous tile: lgkmcnt(0) first.
+  const int n = w1 - w0;
+  if (n > 0) dma_tile(w0, 0);
+  for (int i = 0; i < n; ++i) {
+    if (i + 1 < n) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      dma_tile(w0 + i + 1, (i + 1) & 1);
+      wait_vm<2 * kLoads>();
+    } else {
+      wait_vm<0>();
+    }
+    compute(w0 + i, i & 1);
+  }
+
+  // merge the four waves' partials through LDS (the area overlaps the rings)
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(smem);                       // [wave][q][kMergeStride]
+  float* mml = mo + 4 * 32 * kMergeStride;                           // [wave][q][2]
+  {
+    float* row = mo + (wave * 32 + lr) * kMergeStride;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) row[db * 32 + 8 * (e >> 2) + 4 * lh + (e & 3)] = o[db][e];
+    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    if (lh == 0) {
+      mml[(wave * 32 + lr) * 2] = m_run;
+      mml[(wave * 32 + lr) * 2 + 1] = l;
+    }
+  }
+  __syncthreads();
+  {
+    const int q = tid >> 3, dc = (tid & 7) * 16;
+    const bool ok = decode ? q < rep : t0 + q < a.T;
+    if (!ok) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mml[(w * 32 + q) * 2]);
+    float wt[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mml[(w * 32 + q) * 2];
+      wt[w] = mw == -INFINITY ? 0.f : ex2(mw - M);
+      L += wt[w] * mml[(w * 32 + q) * 2 + 1];
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    bf16x8 ob[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += wt[w] * mo[(w * 32 + q) * kMergeStride + dc + j];
+      ob[j >> 3][j & 7] = f2bf(acc * inv);
+    }
+    bf16* dst = decode ? a.out + (int64_t)b * ldq + (int64_t)(head0 + q) * 128 + dc
+                       : a.out + ((int64_t)b * a.T + t0 + q) * ldq + (int64_t)head0 * 128 + dc;
+    *reinterpret_cast<bf16x8*>(dst) = ob[0];
+    *reinterpret_cast<bf16x8*>(dst + 8) = ob[1];
+  }
+}
+
+}  // namespace
+
+hipError_t attn_flash(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.T <= 0) return hipSuccess;
+  const int rep = a.lq / a.lkv;
+  if (a.lkv <= 0 || a.lq % a.lkv != 0 || rep > 32) return hipErrorInvalidValue;
+  const int n_rb = (a.T + 31) / 32;
+  const int64_t blocks = a.T == 1 ? (int64_t)a.B * a.lkv : (int64_t)a.B * a.lq * n_rb;
+  attn_flash_kernel<<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
+  return hipGetLastError();
+}
+
+}  // namespace tps

@@ -18,10 +18,10 @@
 //    ds_read_b64_tr_b16: in each 16-lane group, source lane s reads 4 d of
 //    key base + s/4 and lane i receives d = dbase + i of keys base .. base+3;
 //  * the softmax runs in the exp2 domain with a running max per query.
-// Early query blocks need few keys.  When the blocks alone cannot fill the
-// GPU, each block's key range is cut into chunks of `chunk` tiles; every
-// chunk leaves a partial (unnormalised O, max, sum) that a second kernel
-// merges in chunk order.
+// Early query blocks need few keys; heavy (late) blocks are launched first.
+// This kernel serves prefills whose blocks alone fill the GPU; smaller ones
+// go to the one-pass kernel of attn_flash.hip, which splits each block's
+// keys among its waves instead.
 #include <type_traits>
 
 #include "common.h"
@@ -78,25 +78,12 @@ struct PrefillPlan {
   int rows;       // query rows per workgroup (32 per wave row block)
   int n_rb;       // query row blocks
   int hgroups;    // workgroups per kv head along the q heads
-  int chunk;      // key tiles per work item; 0: a block's whole key range
-  int items;      // work items per (batch, kv head, head group)
 };
 
 __host__ __device__ inline int rb_tiles(int T, int past, int rows, int r) {
   const int end = (r + 1) * rows < T ? (r + 1) * rows : T;
   return (past + end + kKeys - 1) / kKeys;
 }
-__host__ __device__ inline int rb_chunks(int T, int past, const PrefillPlan& p, int r) {
-  return p.chunk == 0 ? 1 : (rb_tiles(T, past, p.rows, r) + p.chunk - 1) / p.chunk;
-}
-// work items of a (batch, kv head, head group) run heaviest block first:
-// block n_rb - 1 chunks 0 .. , then block n_rb - 2, ...
-__device__ inline int item_base(int T, int past, const PrefillPlan& p, int r) {
-  int acc = 0;
-  for (int rr = p.n_rb - 1; rr > r; --rr) acc += rb_chunks(T, past, p, rr);
-  return acc;
-}
-
 template <int HW, int HG, int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
@@ -119,20 +106,8 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
   const int hgrp = grp % p.hgroups;
   const int kvh = (grp / p.hgroups) % a.lkv;
   const int b = grp / (p.hgroups * a.lkv);
-  int r = p.n_rb - 1 - w, c = 0;
-  if (p.chunk != 0) {
-    int acc = 0;
-    for (r = p.n_rb - 1; r > 0; --r) {
-      const int ch = rb_chunks(a.T, a.past, p, r);
-      if (w < acc + ch) break;
-      acc += ch;
-    }
-    c = w - acc;
-  }
-  const int nt = rb_tiles(a.T, a.past, p.rows, r);
-  const int kt0 = p.chunk != 0 ? c * p.chunk : 0;
-  const int kt1 = p.chunk != 0 ? min(nt, kt0 + p.chunk) : nt;
-  const bool split = p.chunk != 0 && rb_chunks(a.T, a.past, p, r) > 1;
+  const int r = p.n_rb - 1 - w;                           // heaviest blocks first
+  const int kt0 = 0, kt1 = rb_tiles(a.T, a.past, p.rows, r);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
@@ -330,106 +305,38 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
     unsigned char* base = ri < 4 ? smem0 : smem1;
     return reinterpret_cast<bf16*>(base + (ri & 3) * (32 * 128 * 2));
   };
-  if (!split) {
-    // normalise; stage [32 q][128 d] per (wave, head) through LDS, then
-    // write whole 16-byte chunks of each row
-    __syncthreads();   // the staging area overlaps the ring
-#pragma unroll
-    for (int hw = 0; hw < HW; ++hw) {
-      const float l = l_run[hw] + __shfl_xor(l_run[hw], 32, 64);
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      bf16* so = stage_region(wave * HW + hw);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int d = db * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          so[lr * 128 + (((d >> 3) ^ (lr & 15)) << 3) + (d & 7)] = f2bf(o[hw][db][e] * inv);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    if (!active) return;
-#pragma unroll
-    for (int hw = 0; hw < HW; ++hw) {
-      const bf16* so = stage_region(wave * HW + hw);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = lane + i * 64, row = q >> 4, cc = q & 15;
-        const int t = t0w + row;
-        if (t < a.T) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(so + row * 128 + ((cc ^ (row & 15)) << 3));
-          *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.T + t) * ldq + (int64_t)(head0 + hw) * 128 + cc * 8) = v;
-        }
-      }
-    }
-    return;
-  }
-  // split: unnormalised O and (max, sum) per row for the merge kernel
-  if (!active) return;
-  const int64_t item = (int64_t)grp * p.items + w;
-  const int64_t n_items = (int64_t)groups * p.items;
-  float* po = a.scratch;
-  float2* pml = reinterpret_cast<float2*>(a.scratch + n_items * WGH * p.rows * 128);
+  // normalise; stage [32 q][128 d] per (wave, head) through LDS, then
+  // write whole 16-byte chunks of each row
+  __syncthreads();   // the staging area overlaps the ring
 #pragma unroll
   for (int hw = 0; hw < HW; ++hw) {
-    const int wh = hg * HW + hw;
-    const int row = rr * 32 + lr;
-    float* dst = po + ((item * WGH + wh) * p.rows + row) * 128;
+    const float l = l_run[hw] + __shfl_xor(l_run[hw], 32, 64);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* so = stage_region(wave * HW + hw);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int d = db * 32 + 8 * e4 + 4 * lh;
-        *reinterpret_cast<f32x4*>(dst + d) =
-            f32x4{o[hw][db][e4 * 4], o[hw][db][e4 * 4 + 1], o[hw][db][e4 * 4 + 2], o[hw][db][e4 * 4 + 3]};
+      for (int e = 0; e < 16; ++e) {
+        const int d = db * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        so[lr * 128 + (((d >> 3) ^ (lr & 15)) << 3) + (d & 7)] = f2bf(o[hw][db][e] * inv);
       }
-    const float l = l_run[hw] + __shfl_xor(l_run[hw], 32, 64);
-    if (lh == 0) pml[(item * WGH + wh) * p.rows + row] = float2{m_run[hw], l};
   }
-}
-
-// Merges the chunk partials of split row blocks, one thread per (row, head,
-// 4 d): O = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i with m = max_i m_i,
-// summed in chunk order.
-template <int WGH>
-__global__ __launch_bounds__(256) void attn_prefill_merge(AttnArgs a, PrefillPlan p) {
-  const int groups = a.B * a.lkv * p.hgroups;
-  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int dc = (int)(gid & 31);
-  gid >>= 5;
-  const int row = (int)(gid % p.rows);
-  gid /= p.rows;
-  const int wh = (int)(gid % WGH);
-  gid /= WGH;
-  const int grp = (int)(gid % groups);
-  const int r = (int)(gid / groups);
-  if (r >= p.n_rb) return;
-  const int t = r * p.rows + row;
-  const int n = rb_chunks(a.T, a.past, p, r);
-  if (n <= 1 || t >= a.T) return;
-  const int hgrp = grp % p.hgroups;
-  const int kvh = (grp / p.hgroups) % a.lkv;
-  const int b = grp / (p.hgroups * a.lkv);
-  const int64_t first = (int64_t)grp * p.items + item_base(a.T, a.past, p, r);
-  const int64_t n_items = (int64_t)groups * p.items;
-  const float* po = a.scratch;
-  const float2* pml = reinterpret_cast<const float2*>(a.scratch + n_items * WGH * p.rows * 128);
-  float m = -INFINITY;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, pml[((first + i) * WGH + wh) * p.rows + row].x);
-  float l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < n; ++i) {
-    const float2 ml = pml[((first + i) * WGH + wh) * p.rows + row];
-    const float wgt = ml.x == -INFINITY ? 0.f : ex2(ml.x - m);
-    l += wgt * ml.y;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(po + (((first + i) * WGH + wh) * p.rows + row) * 128 + dc * 4);
-    acc += wgt * v;
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+  if (!active) return;
+#pragma unroll
+  for (int hw = 0; hw < HW; ++hw) {
+    const bf16* so = stage_region(wave * HW + hw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = lane + i * 64, row = q >> 4, cc = q & 15;
+      const int t = t0w + row;
+      if (t < a.T) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(so + row * 128 + ((cc ^ (row & 15)) << 3));
+        *reinterpret_cast<u32x4*>(a.out + ((int64_t)b * a.T + t) * ldq + (int64_t)(head0 + hw) * 128 + cc * 8) = v;
+      }
+    }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const bf16x4 ob = {f2bf(acc[0] * inv), f2bf(acc[1] * inv), f2bf(acc[2] * inv), f2bf(acc[3] * inv)};
-  const int head = kvh * (a.lq / a.lkv) + hgrp * WGH + wh;
-  *reinterpret_cast<bf16x4*>(a.out + ((int64_t)b * a.T + t) * a.lq * 128 + (int64_t)head * 128 + dc * 4) = ob;
 }
 
 constexpr int kStages = 3;
@@ -441,58 +348,34 @@ void prefill_shape(int rep, int* hw, int* hg) {
   *hg = g < 4 ? g : 4;
 }
 
-PrefillPlan prefill_plan(int B, int T, int past, int lq, int lkv) {
+PrefillPlan prefill_plan(int B, int T, int lq, int lkv) {
   int hw, hg;
   prefill_shape(lq / lkv, &hw, &hg);
   PrefillPlan p{};
   p.rows = 32 * (4 / hg);
   p.n_rb = (T + p.rows - 1) / p.rows;
   p.hgroups = lq / lkv / (hw * hg);
-  p.chunk = 0;
-  p.items = p.n_rb;
-  const int64_t groups = (int64_t)B * lkv * p.hgroups;
-  if (groups * p.n_rb >= 256) return p;
-  // cut key ranges so that about one work item per CU exists, each of at
-  // least two tiles
-  int64_t total = 0;
-  for (int r = 0; r < p.n_rb; ++r) total += rb_tiles(T, past, p.rows, r);
-  total *= groups;
-  int chunk = (int)((total + 255) / 256);
-  if (chunk < 2) chunk = 2;
-  PrefillPlan q = p;
-  q.chunk = chunk;
-  q.items = 0;
-  for (int r = 0; r < p.n_rb; ++r) q.items += rb_chunks(T, past, q, r);
-  return q.items > p.n_rb ? q : p;
+  return p;
 }
 
 template <int HW, int HG>
 hipError_t launch(const AttnArgs& a, const PrefillPlan& p, hipStream_t s) {
   const int64_t groups = (int64_t)a.B * a.lkv * p.hgroups;
-  attn_prefill_kernel<HW, HG, kStages><<<(unsigned)(groups * p.items), 256, 0, s>>>(a, p);
-  if (p.chunk != 0) {
-    const int64_t threads = groups * p.n_rb * (HW * HG) * p.rows * 32;
-    attn_prefill_merge<HW * HG><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a, p);
-  }
+  attn_prefill_kernel<HW, HG, kStages><<<(unsigned)(groups * p.n_rb), 256, 0, s>>>(a, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t attn_prefill_scratch_bytes(int B, int T, int past, int lq, int lkv) {
-  if (B <= 0 || T <= 0 || lkv <= 0) return 0;
-  const PrefillPlan p = prefill_plan(B, T, past, lq, lkv);
-  if (p.chunk == 0) return 0;
-  int hw, hg;
-  prefill_shape(lq / lkv, &hw, &hg);
-  const int64_t items = (int64_t)B * lkv * p.hgroups * p.items;
-  return (size_t)items * hw * hg * p.rows * (128 + 2) * sizeof(float);
+bool attn_prefill_fills(int B, int T, int lq, int lkv) {
+  if (B <= 0 || T <= 0 || lkv <= 0) return false;
+  const PrefillPlan p = prefill_plan(B, T, lq, lkv);
+  return (int64_t)B * lkv * p.hgroups * p.n_rb >= 256;
 }
 
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
-  const PrefillPlan p = prefill_plan(a.B, a.T, a.past, a.lq, a.lkv);
-  if (p.chunk != 0 && a.scratch == nullptr) return hipErrorInvalidValue;
+  const PrefillPlan p = prefill_plan(a.B, a.T, a.lq, a.lkv);
   switch (a.lq / a.lkv) {
     case 1: return launch<1, 1>(a, p, s);
     case 2: return launch<2, 1>(a, p, s);

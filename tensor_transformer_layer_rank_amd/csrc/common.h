@@ -82,12 +82,14 @@ struct AttnArgs {
   const bf16* k_cache;   // [B, lkv, S_max, 128]
   const bf16* v_cache;
   bf16* out;             // [B*T, lq*128]
-  float* scratch;        // split partials (decode: KV splits; prefill: key chunks)
   int B, T, past, S_max, lq, lkv;
 };
-size_t attn_decode_scratch_bytes(int B, int lq, int lkv, int ctx);
-size_t attn_prefill_scratch_bytes(int B, int T, int past, int lq, int lkv);
-hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
+// Prefill kernel whose workgroups each cover a (kv head, row block) with all
+// its q heads; used when those workgroups alone fill the GPU.
+bool attn_prefill_fills(int B, int T, int lq, int lkv);
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
+// One-pass flash attention for decode (rows = the q heads of a kv head) and
+// for the prefills that attn_prefill would leave the GPU short of work.
+hipError_t attn_flash(const AttnArgs& a, hipStream_t s);
 
 }  // namespace tps

@@ -70,13 +70,6 @@ AttnWs attn_ws(const tp_cfg* c, const tp_local& L, int64_t B, int64_t T, int64_t
   size_t sb = gemm_scratch_bytes(M, L.n_qkv, c->hidden, EPI_QKV);
   const size_t so = gemm_scratch_bytes(M, c->hidden, (int64_t)L.lq * 128, EPI_BF16);
   if (so > sb) sb = so;
-  if (T == 1 && B > 0) {
-    const size_t sd = attn_decode_scratch_bytes((int)B, L.lq, L.lkv, (int)(past + 1));
-    if (sd > sb) sb = sd;
-  } else if (T > 1 && B > 0) {
-    const size_t sp = attn_prefill_scratch_bytes((int)B, (int)T, (int)past, L.lq, L.lkv);
-    if (sp > sb) sb = sp;
-  }
   w.scratch_bytes = align_up(sb);
   w.total = w.scratch + w.scratch_bytes;
   return w;
@@ -250,8 +243,8 @@ int tp_qkv_attn(const tp_cfg* cfg, const void* x, int32_t B, int32_t T, int32_t 
   if (e != hipSuccess) return TP_ERR_LAUNCH;
   // 2. attention over the local heads
   AttnArgs aa{q, static_cast<const bf16*>(k_cache), static_cast<const bf16*>(v_cache), attn,
-              reinterpret_cast<float*>(scratch), B, T, past_len, S_max, L.lq, L.lkv};
-  e = T == 1 ? attn_decode(aa, s) : attn_prefill(aa, s);
+              B, T, past_len, S_max, L.lq, L.lkv};
+  e = T > 1 && attn_prefill_fills(B, T, L.lq, L.lkv) ? attn_prefill(aa, s) : attn_flash(aa, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
   // 3. row-parallel o_proj -> partial sum
   GemmProblem go{attn, static_cast<const bf16*>(w_o), out_partial, M, H, lqd, lqd, lqd, H, 0};

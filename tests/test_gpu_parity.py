@@ -385,12 +385,26 @@ def check_attn(w, wid, r, B, T, past, S_max, rows=None, Wg=None, W=None, tol=TOL
     return rk, kc, vc, part
 
 
+def test_qkv_attn_wide_prefill_sampled():
+    """A prefill whose (kv head, row block) workgroups fill the GPU by
+    themselves runs the GQA-sharing prefill kernel: 17 sequences of 1000
+    tokens (ragged last row block), sampled rows of every sequence."""
+    w, wid = MID["rep2"], MID_WID["rep2"]
+    B, T = 17, 1000
+    rows = np.unique(np.concatenate([[0, 127, 128, T - 1, T, B * T - 1],
+                                     np.random.default_rng(5).integers(0, B * T, 24)]))
+    for r in range(w["tp"]):
+        check_attn(w, wid, r, B, T, 0, T + 8, rows=rows)
+
+
 @pytest.mark.parametrize("name", list(MID))
 @pytest.mark.parametrize("phase", ["prefill", "prefill-after-past", "decode", "decode-ctx1", "decode-long"])
 def test_qkv_attn_mid(name, phase):
-    """decode: 8 sequences (head-split blocks when rep >= 8); decode-ctx1:
-    3 sequences, one key; decode-long: 2 sequences at context 3000, which
-    splits the keys and merges the splits."""
+    """prefill: 2 sequences of 300 tokens; prefill-after-past: 77 new tokens
+    after 150 cached ones; decode: 8 sequences; decode-ctx1: 3 sequences, one
+    key; decode-long: 2 sequences at context 3000 (the key range split among
+    a block's waves and merged).  These grids are small, so the one-pass
+    flash kernel runs every phase."""
     w, wid = MID[name], MID_WID[name]
     W = synth.full_weights(wid, w)
     Wg = {k: v.to(DEV) for k, v in W.items()}
