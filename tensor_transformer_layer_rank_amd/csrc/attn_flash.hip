@@ -35,12 +35,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kKeys = 32;                    // keys per tile
 constexpr int kTileB = kKeys * 256;          // bytes of one K or V tile
 constexpr int kStageB = 2 * kTileB;          // K tile, then V tile
-constexpr int kWaveRingB = 2 * kStageB;      // two stages per wave
 constexpr int kLoads = kTileB / 1024;        // 1 KB direct-to-LDS loads per tile (K or V)
 constexpr int kMergeStride = 129;            // floats per merged row (odd: no bank conflicts)
 constexpr float kQScale = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
 constexpr float kSlack = 8.f;                 // lazy-rescale margin, log2 units
-static_assert(4 * 32 * (kMergeStride + 2) * 4 <= 4 * kWaveRingB, "merge area fits the rings");
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // byte offset of 16-byte chunk c (d = 8c .. 8c+7) of key row `key` in a tile
@@ -71,9 +69,16 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
                : "memory");
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NWV waves per workgroup, NST ring stages per wave (NST - 1 tiles in
+// flight while one is computed).
+template <int NWV, int NST>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_flash_kernel(AttnArgs a, int n_rb) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kWaveRingB];
+  constexpr int NT = NWV * 64;
+  constexpr int kWaveRingB = NST * kStageB;
+  static_assert(NWV * kWaveRingB <= 163840, "rings fit the CU's LDS");
+  static_assert(NWV * 32 * (kMergeStride + 2) * 4 <= NWV * kWaveRingB, "merge area fits the rings");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NWV * kWaveRingB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,7 +108,7 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   const int min_pos = a.past + t0;                        // the block's first query position
   const int n_keys = decode ? a.past + 1 : a.past + min(a.T, t0 + 32);
   const int nt = (n_keys + kKeys - 1) / kKeys;
-  const int w0 = wave * nt / 4, w1 = (wave + 1) * nt / 4;   // this wave's tiles
+  const int w0 = wave * nt / NWV, w1 = (wave + 1) * nt / NWV;   // this wave's tiles
 
   // Q^T operands: lane supplies q[row lr, ks*16 + lh*8 .. +8]
   bf16x8 qf[8];
@@ -214,26 +219,26 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
       }
   };
 
-  // this wave's ring: tile w0 + i lives in stage i % 2; the next tile's
-  // loads go out before the current one is computed.  The stage a load
+  // this wave's ring: tile w0 + i lives in stage i % NST; tiles up to
+  // i + NST - 1 are in flight while tile i is computed.  The stage a load
   // refills was read by the previous tile: lgkmcnt(0) first.
   const int n = w1 - w0;
-  if (n > 0) dma_tile(w0, 0);
+  for (int j = 0; j < NST - 1 && j < n; ++j) dma_tile(w0 + j, j);
   for (int i = 0; i < n; ++i) {
-    if (i + 1 < n) {
+    if (i + NST - 1 < n) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      dma_tile(w0 + i + 1, (i + 1) & 1);
-      wait_vm<2 * kLoads>();
+      dma_tile(w0 + i + NST - 1, (i + NST - 1) % NST);
+      wait_vm<(NST - 1) * 2 * kLoads>();
     } else {
       wait_vm<0>();
     }
-    compute(w0 + i, i & 1);
+    compute(w0 + i, i % NST);
   }
 
   // merge the four waves' partials through LDS (the area overlaps the rings)
   __syncthreads();
   float* mo = reinterpret_cast<float*>(smem);                       // [wave][q][kMergeStride]
-  float* mml = mo + 4 * 32 * kMergeStride;                           // [wave][q][2]
+  float* mml = mo + NWV * 32 * kMergeStride;                         // [wave][q][2]
   {
     float* row = mo + (wave * 32 + lr) * kMergeStride;
 #pragma unroll
@@ -248,32 +253,35 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   }
   __syncthreads();
   {
-    const int q = tid >> 3, dc = (tid & 7) * 16;
+    constexpr int TPR = NT / 32, DPT = 128 / TPR;           // threads per row, d per thread
+    const int q = tid / TPR, dc = (tid % TPR) * DPT;
     const bool ok = decode ? q < rep : t0 + q < a.T;
     if (!ok) return;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mml[(w * 32 + q) * 2]);
-    float wt[4], L = 0.f;
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, mml[(w * 32 + q) * 2]);
+    float wt[NWV], L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       const float mw = mml[(w * 32 + q) * 2];
       wt[w] = mw == -INFINITY ? 0.f : ex2(mw - M);
       L += wt[w] * mml[(w * 32 + q) * 2 + 1];
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    bf16x8 ob[2];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc += wt[w] * mo[(w * 32 + q) * kMergeStride + dc + j];
-      ob[j >> 3][j & 7] = f2bf(acc * inv);
-    }
     bf16* dst = decode ? a.out + (int64_t)b * ldq + (int64_t)(head0 + q) * 128 + dc
                        : a.out + ((int64_t)b * a.T + t0 + q) * ldq + (int64_t)head0 * 128 + dc;
-    *reinterpret_cast<bf16x8*>(dst) = ob[0];
-    *reinterpret_cast<bf16x8*>(dst + 8) = ob[1];
+#pragma unroll
+    for (int c = 0; c < DPT / 8; ++c) {
+      bf16x8 ob;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) acc += wt[w] * mo[(w * 32 + q) * kMergeStride + dc + 8 * c + j];
+        ob[j] = f2bf(acc * inv);
+      }
+      *reinterpret_cast<bf16x8*>(dst + 8 * c) = ob;
+    }
   }
 }
 
@@ -285,7 +293,7 @@ hipError_t attn_flash(const AttnArgs& a, hipStream_t s) {
   if (a.lkv <= 0 || a.lq % a.lkv != 0 || rep > 32) return hipErrorInvalidValue;
   const int n_rb = (a.T + 31) / 32;
   const int64_t blocks = a.T == 1 ? (int64_t)a.B * a.lkv : (int64_t)a.B * a.lq * n_rb;
-  attn_flash_kernel<<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
+  attn_flash_kernel<4, 2><<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
   return hipGetLastError();
 }
 
