@@ -178,6 +178,49 @@ def lm_head(x, table_local, store=bf16):
     return store(np.asarray(x, np.float64) @ np.asarray(table_local, np.float64).T)
 
 
+# Greedy decode over vocab-parallel logits ([TPS] Implementation: the next
+# token is the argmax of the last position's logits after the all-gather of
+# every rank's slice; argmax takes the first index of the maximum).  Per
+# shard: the (max, first global index of it) of the local slice; the shards'
+# candidates then combine to the max, ties going to the smaller global index,
+# which is the first maximum of the concatenated logits.
+
+def lm_head_argmax(x, table_local, vocab_start, store=bf16):
+    """(values [M], global indices [M]) of this shard's local logits."""
+    logits = lm_head(x, table_local, store)
+    if logits.shape[1] == 0:
+        return np.full(logits.shape[0], -np.inf), np.full(logits.shape[0], -1, np.int64)
+    vals = np.empty(logits.shape[0])
+    idx = np.empty(logits.shape[0], np.int64)
+    for m in range(logits.shape[0]):
+        best = 0
+        for n in range(1, logits.shape[1]):
+            if logits[m, n] > logits[m, best]:
+                best = n
+        vals[m], idx[m] = logits[m, best], vocab_start + best
+    return vals, idx
+
+
+def argmax_combine(vals, idx):
+    """vals, idx: [n_shards, M] candidates.  Per row the largest value; among
+    equal values the smallest global index; shards with no vocabulary carry
+    (-inf, -1) and never win."""
+    vals = np.asarray(vals, np.float64)
+    idx = np.asarray(idx, np.int64)
+    out_v = np.empty(vals.shape[1])
+    out_i = np.empty(vals.shape[1], np.int64)
+    for m in range(vals.shape[1]):
+        bv, bi = -np.inf, -1
+        for r in range(vals.shape[0]):
+            v, i = vals[r, m], idx[r, m]
+            if i < 0:
+                continue
+            if bi < 0 or v > bv or (v == bv and i < bi):
+                bv, bi = v, i
+        out_v[m], out_i[m] = bv, bi
+    return out_v, out_i
+
+
 # --------------------------------------------------------------------------
 # attention block pieces   ([TPS] Implementation, TPAttention.forward)
 # --------------------------------------------------------------------------

@@ -430,3 +430,64 @@ def test_lm_head_matches_linear_and_concats():
         parts.append(O.lm_head(x, O.shard(c, O.W_VOCAB, E), store=_ident))
     ref = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(E)).numpy()
     np.testing.assert_allclose(np.concatenate(parts, 1), ref, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------ greedy argmax over shards
+
+def _sharded_argmax(x, E, V, H, n):
+    vals, idx = [], []
+    for r in range(n):
+        c = O.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        L = O.local_dims(c)
+        v, i = O.lm_head_argmax(x, O.shard(c, O.W_VOCAB, E), L.vocab_start)
+        vals.append(v)
+        idx.append(i)
+    return O.argmax_combine(np.stack(vals), np.stack(idx))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
+def test_sharded_argmax_equals_torch_argmax_of_gathered_logits(n):
+    """Per-shard (max, first index) plus the combine equals torch.argmax over
+    the all-gathered, bf16-stored logits (uneven last shard at n = 3, 8)."""
+    V, H, M = 1000, 64, 12
+    E = O.bf16(_rand(80, (V, H), 0.02))
+    x = O.bf16(_rand(81, (M, H)))
+    v, i = _sharded_argmax(x, E, V, H, n)
+    full = torch.from_numpy(O.bf16(x @ E.T))
+    ref_v, ref_i = full.max(dim=1)
+    assert np.array_equal(i, torch.argmax(full, dim=1).numpy())
+    assert np.array_equal(i, ref_i.numpy())
+    np.testing.assert_array_equal(v, ref_v.numpy())
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_sharded_argmax_ties_go_to_the_first_index(n):
+    """Planted ties across and inside shards: the winner is the smallest
+    global index holding the maximum (torch.argmax and a plain scan agree)."""
+    V, H, M = 40, 8, 6
+    rng = np.random.default_rng(82)
+    E = O.bf16(rng.standard_normal((V, H)) * 0.1)
+    for dup in (3, 17, 18, 31, 39):       # identical rows in several shards
+        E[dup] = E[25]
+    x = O.bf16(rng.standard_normal((M, H)))
+    x[0] = 0.0                            # every logit 0: index 0 wins
+    E[:, :] = np.where(np.arange(V)[:, None] == 7, E[25], E)    # one more copy
+    v, i = _sharded_argmax(x, E, V, H, n)
+    logits = O.bf16(x @ E.T)
+    for m in range(M):
+        best = 0
+        for k in range(V):
+            if logits[m, k] > logits[m, best]:
+                best = k
+        assert i[m] == best and v[m] == logits[m, best]
+    assert i[0] == 0
+    assert np.array_equal(i, torch.argmax(torch.from_numpy(logits), dim=1).numpy())
+
+
+def test_argmax_combine_skips_empty_shards():
+    """V = 5 over 4 ranks leaves the last shard empty; it never wins."""
+    V, H, n = 5, 4, 4
+    E = O.bf16(_rand(83, (V, H)))
+    x = O.bf16(_rand(84, (3, H)))
+    v, i = _sharded_argmax(x, E, V, H, n)
+    assert np.array_equal(i, np.argmax(O.bf16(x @ E.T), axis=1))
