@@ -10,6 +10,8 @@ One step runs every row of the hot path once, on rank 0, in this order:
   prefill tp_qkv_attn (B=1, T tokens, empty cache) + tp_mlp (T rows)
   lm_head tp_lm_head over the id rows (the vocab slice of the logits)
   decode  tp_qkv_attn (B sequences, 1 token, context c) + tp_mlp (B rows)
+  decode_argmax  tp_lm_head_argmax over the B decode rows (this rank's greedy
+          candidates over its vocab slice)
 HIP events on the launch stream bracket each phase.  `value` is the layer's
 prefill throughput (TFLOP/s of the prefill phase); decode GB/s, the lm_head
 TFLOP/s and the other phases are reported beside it.  Inputs are synthetic,
@@ -110,6 +112,8 @@ class Set:
         self.d_attn = torch.empty(B, H, dtype=bf, device=dev)
         self.d_mlp = torch.empty(B, H, dtype=bf, device=dev)
         self.logits = torch.empty(n_ids, L.vocab_end - L.vocab_start, dtype=bf, device=dev)
+        self.tok_val = torch.empty(B, dtype=torch.float32, device=dev)
+        self.tok_idx = torch.empty(B, dtype=torch.int32, device=dev)
 
     def nbytes(self):
         import torch
@@ -159,11 +163,12 @@ def run_bench(args):
     ws_attn_d = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_ATTN, B, 1, ctx - 1), dtype=torch.uint8, device=dev)
     ws_mlp = torch.empty(max(tp.tp_workspace_bytes(c, tp.TP_OP_MLP, T, 1), tp.tp_workspace_bytes(c, tp.TP_OP_MLP, B, 1)),
                          dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_LM_ARGMAX, B, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     kinds = ((tp.TP_W_Q, "q", "qkv"), (tp.TP_W_K, "k", "qkv"), (tp.TP_W_V, "v", "qkv"), (tp.TP_W_O, "o", "o"),
              (tp.TP_W_GATE, "gate", "gu"), (tp.TP_W_UP, "up", "gu"), (tp.TP_W_DOWN, "down", "down"))
-    phases = ["shard", "embed", "prefill", "lm_head", "decode"]
+    phases = ["shard", "embed", "prefill", "lm_head", "decode", "decode_argmax"]
 
     def step(s: Set, ev=None):
         rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
@@ -184,11 +189,13 @@ def run_bench(args):
                        s.vc_dec, ctx, s.d_attn, ws_attn_d)
         tp.tp_mlp(c, s.x_dec, B, s.gu, s.down, s.d_mlp, ws_mlp)
         rec(5)
+        tp.tp_lm_head_argmax(c, s.x_dec, B, s.vocab, s.tok_val, s.tok_idx, ws_lm)
+        rec(6)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -209,6 +216,9 @@ def run_bench(args):
     nv = L.vocab_end - L.vocab_start
     in_shard = int(((src_ids := sets[0].ids.cpu()) >= L.vocab_start).logical_and(src_ids < L.vocab_end).sum())
     emb_bytes = 4 * n_ids + 2 * H * in_shard + 2 * H * n_ids
+    # greedy decode head: the vocab slice and the decode rows are read once;
+    # one (value, id) pair per row is written
+    argmax_bytes = 2 * nv * H + 2 * B * H + 8 * B
     shard_bytes = 2 * 2 * (L.n_qkv * H + H * L.lq * 128 + 2 * L.li * H + H * L.li + nv * H)
 
     prefill_tflops = prefill_flops / ph["prefill"] / 1e12
@@ -238,6 +248,8 @@ def run_bench(args):
         "decode_pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
         "lm_head_TFLOPs": round(lm_tflops, 1),
         "lm_head_pct_mfma_peak": round(100 * lm_tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "decode_argmax_GBps": round(argmax_bytes / ph["decode_argmax"] / 1e9, 1),
+        "decode_argmax_pct_hbm_peak": round(100 * argmax_bytes / ph["decode_argmax"] / 1e9 / HBM_PEAK_GBPS, 2),
         "embed_GBps": round(emb_bytes / ph["embed"] / 1e9, 1),
         "shard_GBps": round(shard_bytes / ph["shard"] / 1e9, 1),
         "phase_us": {p: round(v * 1e6, 2) for p, v in ph.items()},

@@ -67,7 +67,7 @@ typedef enum {
   TP_W_GATE = 4, TP_W_UP = 5, TP_W_DOWN = 6, TP_W_VOCAB = 7
 } tp_weight_kind;
 
-typedef enum { TP_OP_ATTN = 0, TP_OP_MLP = 1 } tp_op;
+typedef enum { TP_OP_ATTN = 0, TP_OP_MLP = 1, TP_OP_LM_ARGMAX = 2 } tp_op;
 
 /* Model shape and this rank's place in the group ([TPS] "Implementation":
  * every layer is built from the rank and the group size).  48 bytes. */
@@ -114,9 +114,10 @@ typedef struct {
  * embedding and lm_head entry points. */
 int tp_local_dims(const tp_cfg* cfg, tp_local* out);
 
-/* Bytes of device workspace that tp_qkv_attn (op = TP_OP_ATTN) or tp_mlp
- * (op = TP_OP_MLP) needs for B sequences of T new tokens after past_len
- * cached ones (tp_mlp: M = B * T rows; past_len ignored). */
+/* Bytes of device workspace that tp_qkv_attn (op = TP_OP_ATTN), tp_mlp
+ * (op = TP_OP_MLP) or tp_lm_head_argmax (op = TP_OP_LM_ARGMAX) needs for B
+ * sequences of T new tokens after past_len cached ones (tp_mlp and
+ * tp_lm_head_argmax: M = B * T rows; past_len ignored). */
 int tp_workspace_bytes(const tp_cfg* cfg, int op, int64_t B, int64_t T, int64_t past_len,
                        size_t* out_bytes);
 
@@ -203,6 +204,32 @@ int tp_mlp(const tp_cfg* cfg, const void* x, int64_t M, const void* w_gate_up,
  * each sequence's last token) is the caller's choice.  M = 0: no-op. */
 int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local,
                void* logits_local, void* stream);
+
+/* tp_lm_head_argmax -- this rank's greedy candidate per row ([TPS]
+ * "Implementation": decode takes the argmax of the last position's logits;
+ * the vocab-split output layer gives each rank a slice of them).  Instead of
+ * all-gathering V logits per row, the rank reduces its slice:
+ *   logits = bf16(x @ vocab_local^T)            as tp_lm_head stores them
+ *   out_val[m] = max_n logits[m, n]             (fp32 holding the bf16 value)
+ *   out_idx[m] = vocab_start + first n attaining it (a global token id)
+ * An empty vocab slice gives (-inf, -1).  The candidates of all ranks
+ * (gathered into [n_shards, M]) combine with tp_argmax_combine.
+ * x: bf16 [M, H]; vocab_local: bf16 [vocab_end - vocab_start, H];
+ * out_val: float [M]; out_idx: int32 [M];
+ * workspace >= tp_workspace_bytes(cfg, TP_OP_LM_ARGMAX, M, 1, 0) (it holds the
+ * local logits).  Requires TP_BF16 (TP_ERR_DTYPE) and H % 8 == 0.  M = 0: no-op. */
+int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local,
+                      float* out_val, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+
+/* tp_argmax_combine -- the cross-shard step of the greedy argmax: per row the
+ * candidate with the largest value, ties to the smallest token id (the first
+ * maximum of the concatenated logits, as argmax takes it); candidates with
+ * idx < 0 (empty shards) never win.  vals: float [n_shards, M]; idx: int32
+ * [n_shards, M] (each rank's tp_lm_head_argmax outputs, gathered); out_idx:
+ * int32 [M]; out_val_opt: float [M] or NULL.  n_shards >= 1 (TP_ERR_RANGE).
+ * Pointers 4-byte aligned (TP_ERR_ALIGN).  M = 0: no-op. */
+int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, int64_t M,
+                      int32_t* out_idx, float* out_val_opt, void* stream);
 
 #ifdef __cplusplus
 }

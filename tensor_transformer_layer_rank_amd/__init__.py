@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libtpshard.so")
 
 TP_F32, TP_BF16 = 0, 1
 TP_W_Q, TP_W_K, TP_W_V, TP_W_O, TP_W_GATE, TP_W_UP, TP_W_DOWN, TP_W_VOCAB = range(8)
-TP_OP_ATTN, TP_OP_MLP = 0, 1
+TP_OP_ATTN, TP_OP_MLP, TP_OP_LM_ARGMAX = 0, 1, 2
 
 EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_shard_weights", "tp_embed_vocab",
-           "tp_qkv_attn", "tp_mlp", "tp_lm_head")
+           "tp_qkv_attn", "tp_mlp", "tp_lm_head", "tp_lm_head_argmax", "tp_argmax_combine")
 
 
 class TpError(RuntimeError):
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.tp_qkv_attn.argtypes = [C, P, I32, I32, I32, P, P, P, P, P, P, I32, P, P, P, P, SZ, P]
         L.tp_mlp.argtypes = [C, P, I64, P, P, P, P, P, SZ, P]
         L.tp_lm_head.argtypes = [C, P, I64, P, P, P]
+        L.tp_lm_head_argmax.argtypes = [C, P, I64, P, P, P, P, SZ, P]
+        L.tp_argmax_combine.argtypes = [P, P, I32, I64, P, P, P]
         for name in EXPORTS:
             if name != "tp_status_str":
                 getattr(L, name).restype = ctypes.c_int
@@ -167,3 +169,13 @@ def tp_mlp(cfg: Cfg, x, M: int, w_gate_up, w_down, out_partial, workspace, h_out
 def tp_lm_head(cfg: Cfg, x, M: int, vocab_local, logits_local, stream=None):
     _check(lib().tp_lm_head(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(vocab_local), _ptr(logits_local),
                             _stream(stream)))
+
+
+def tp_lm_head_argmax(cfg: Cfg, x, M: int, vocab_local, out_val, out_idx, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tp_lm_head_argmax(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(vocab_local), _ptr(out_val), _ptr(out_idx),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_argmax_combine(vals, idx, n_shards: int, M: int, out_idx, out_val=None, stream=None):
+    _check(lib().tp_argmax_combine(_ptr(vals), _ptr(idx), n_shards, M, _ptr(out_idx), _ptr(out_val), _stream(stream)))

@@ -27,7 +27,9 @@ enum GemmEpi {
   EPI_BF16 = 0,       // C bf16 [M, N] (row stride ldc)
   EPI_F32 = 1,        // C fp32 [M, N]; with split-K: partials [splits, M, N]
   EPI_SILU_BF16 = 2,  // B = [gate; up] with `li` rows each; C = silu(gate)*up, bf16 [M, li]
-  EPI_QKV = 3         // merged q/k/v projection finished per head (QkvArgs); C unused
+  EPI_QKV = 3,        // merged q/k/v projection finished per head (QkvArgs); C unused
+  EPI_ARGMAX = 4      // per row and N tile: (max of the bf16-rounded values, first column);
+                      // C = 8-byte candidates [M, tiles_n] (float value, int32 column), ldc = tiles_n
 };
 
 // Per-head finish of the merged QKV projection (row m = b*T + t, N = (lq +
@@ -60,6 +62,8 @@ struct GemmProblem {
 // K is split and fp32 partials in scratch are summed by a second kernel;
 // otherwise (scratch NULL or too small) no split is made.
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int epi);
+// N tiles of the plan gemm_bf16 uses for an EPI_ARGMAX problem (never split)
+int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratch_bytes, hipStream_t s);
 
 // fp32 GEMM (small problems): C = A B^T, or silu-mul of the gate/up halves.
@@ -91,5 +95,15 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 // One-pass flash attention for decode (rows = the q heads of a kv head) and
 // for the prefills that attn_prefill would leave the GPU short of work.
 hipError_t attn_flash(const AttnArgs& a, hipStream_t s);
+
+// --- greedy argmax over vocab-parallel logits ------------------------------
+// out_val[m], out_idx[m] = the best of the n candidates cand[m, 0:n] (8 bytes
+// each: float value, int32 column, column < 0 = none), column + idx0.
+hipError_t argmax_candidates(const void* cand, int64_t M, int64_t n, int64_t idx0, float* out_val, int32_t* out_idx,
+                             hipStream_t s);
+// out_idx[m] = the candidate (vals, idx [n_shards, M]) with the largest
+// value, ties to the smallest index, idx < 0 skipped; out_val optional.
+hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, int64_t M, int32_t* out_idx,
+                          float* out_val, hipStream_t s);
 
 }  // namespace tps

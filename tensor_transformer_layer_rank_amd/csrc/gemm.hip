@@ -370,6 +370,62 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 
   // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
   // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block.
+  if constexpr (EPI == EPI_ARGMAX) {
+    // Greedy-decode candidates: per tile row, the largest bf16-rounded
+    // value over the tile's columns and the first column holding it (ties
+    // to the smaller column, as argmax takes the first maximum); the 32
+    // lanes of a half-wave hold 32 columns of a row, then the WGN waves of
+    // the tile combine through LDS.
+    static_assert(!SPLIT, "argmax candidates come from whole K");
+    __syncthreads();   // the ring is no longer read
+    float* cv = reinterpret_cast<float*>(smem);
+    int* ci = reinterpret_cast<int*>(cv + WGN * BM);
+    auto better = [](float v, int i, float bv, int bi) { return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi)); };
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t col = (int64_t)tn * BN + ncol(j) + lr;
+          const float v = bf2f(f2bf(acc[i][j][e]));
+          if (col < p.N && better(v, (int)col, bv, bi)) {
+            bv = v;
+            bi = (int)col;
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          const float ov = __shfl_xor(bv, off, 64);
+          const int oi = __shfl_xor(bi, off, 64);
+          if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if (lr == 0) {
+          const int r = wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+          cv[wn * BM + r] = bv;
+          ci[wn * BM + r] = bi;
+        }
+      }
+    __syncthreads();
+    u32x2* cand = static_cast<u32x2*>(p.C);
+    for (int r = tid; r < BM; r += NT) {
+      if (m0 + r >= M) continue;
+      float bv = cv[r];
+      int bi = ci[r];
+      for (int w = 1; w < WGN; ++w)
+        if (better(cv[w * BM + r], ci[w * BM + r], bv, bi)) {
+          bv = cv[w * BM + r];
+          bi = ci[w * BM + r];
+        }
+      cand[(m0 + r) * p.ldc + tn] = u32x2{__float_as_uint(bv), (uint32_t)bi};
+    }
+    return;
+  }
   if constexpr (EPI == EPI_QKV) {
     static_assert(qkv_tile_ok(BM, BN, S), "QKV tile must cover whole heads and fit the ring");
     // stage the fp32 tile [BM][BN] in LDS (16-byte chunk c of row r at
@@ -878,13 +934,14 @@ constexpr Variant kVariants[V_COUNT] = {
     {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},
 };
 // Constants fitted to a sweep of every (variant, split) plan over the
-// decode, prefill and lm_head shapes of the Qwen3-0.6B / 32B shards on
-// MI355X (the chosen plans are within 14% of the measured best on average).
-constexpr double kHbmBytesPerUs = 5.0e6;       // sustained weight streaming, bytes per microsecond
+// decode, prefill, lm_head and decode-argmax shapes of the Qwen3-0.6B / 32B
+// shards on MI355X (27 shapes; the chosen plans are within 1% of the
+// measured best on average, 26 us of regret summed over all of them).
+constexpr double kHbmBytesPerUs = 5.5e6;       // sustained weight streaming, bytes per microsecond
 constexpr double kWgBytesPerUs = 3.0e4;        // one workgroup's streaming rate
 constexpr double kLaunchUs = 2.0;
-constexpr double kReduceUs = 4.0;              // the split-K reduction kernel: launch and ramp
-constexpr double kEpiUsPerKB = 0.05;           // tile write-out per resident round
+constexpr double kReduceUs = 5.0;              // the split-K reduction kernel: launch and ramp
+constexpr double kEpiUsPerKB = 0.03;           // tile write-out per resident round
 
 struct Plan { int v; int splits; int64_t kps; int tiles_m, tiles_n; };
 
@@ -906,7 +963,11 @@ double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int
   const double bytes = (double)N * K * 2 + (double)M * K * 2 + partial;
   const double active = (double)(wgs < resident ? wgs : resident);
   const double rate = active * kWgBytesPerUs < kHbmBytesPerUs ? active * kWgBytesPerUs : kHbmBytesPerUs;
-  const double t_mem = bytes / rate * ((double)rounds * resident / (wgs > resident ? wgs : resident));
+  // With at least one workgroup per CU the CUs pull bytes at the aggregate
+  // rate and a partial last round costs little (its CUs share HBM with
+  // fewer neighbours); below that, idle CUs cost their share.
+  const double t_mem = wgs >= kCUs ? bytes / rate
+                                   : bytes / rate * ((double)rounds * resident / (wgs > resident ? wgs : resident));
   // the reduction runs after the GEMM: it reads every partial and writes C
   const double t_red = splits > 1 ? (partial + (double)M * ncols * (epi == EPI_F32 ? 4 : 2)) / kHbmBytesPerUs + kReduceUs : 0.0;
   return (t_comp > t_mem ? t_comp : t_mem) + kLaunchUs + t_red;
@@ -975,6 +1036,10 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   }
   // the planner never picks a variant that cannot run the epilogue
   if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
+  if (epi == EPI_ARGMAX) {
+    gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+    return hipGetLastError();
+  }
   if (epi == EPI_BF16)
     gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   else
@@ -1013,14 +1078,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }  // namespace
 
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int epi) {
-  if (M <= 0 || N <= 0) return 0;
+  if (M <= 0 || N <= 0 || epi == EPI_ARGMAX) return 0;
   const Plan pl = make_plan(M, N, K, epi, true);
   return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
 
+int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0;
+  return make_plan(M, N, K, EPI_ARGMAX, false).tiles_n;
+}
+
 hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratch_bytes, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const bool can_split = scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
+  const bool can_split = epi != EPI_ARGMAX && scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
   const Plan pl = make_plan(p.M, p.N, p.K, epi, can_split);
   // eight or more rounds of 256 x 256 tiles: one persistent workgroup per
   // CU (measured: faster from about that many rounds on, when the per-tile

@@ -93,6 +93,18 @@ MlpWs mlp_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
   return w;
 }
 
+// workspace of tp_lm_head_argmax: one 8-byte candidate per row and N tile
+struct LmWs {
+  int64_t tiles_n;
+  size_t total;
+};
+LmWs lm_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
+  LmWs w{};
+  w.tiles_n = gemm_argmax_tiles_n(M, L.vocab_end - L.vocab_start, c->hidden);
+  w.total = align_up((size_t)(M * w.tiles_n) * 8);
+  return w;
+}
+
 int launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
 
 }  // namespace
@@ -131,6 +143,8 @@ int tp_workspace_bytes(const tp_cfg* cfg, int op, int64_t B, int64_t T, int64_t 
     *out_bytes = attn_ws(cfg, L, B, T, past_len).total;
   } else if (op == TP_OP_MLP) {
     *out_bytes = mlp_ws(cfg, L, B * T).total;
+  } else if (op == TP_OP_LM_ARGMAX) {
+    *out_bytes = lm_ws(cfg, L, B * T).total;
   } else {
     return TP_ERR_KIND;
   }
@@ -307,6 +321,46 @@ int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_lo
                              static_cast<float*>(logits_local), M, N, H, 0, s));
   GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), logits_local, M, N, H, H, H, N, 0};
   return launched(gemm_bf16(g, EPI_BF16, nullptr, 0, s));
+}
+
+int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local, float* out_val,
+                      int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (cfg->vocab == 0 || cfg->hidden % 8) return TP_ERR_SHAPE;
+  if (M < 0) return TP_ERR_RANGE;
+  if (!x || !vocab_local || !out_val || !out_idx) return TP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(vocab_local) || ((uintptr_t)out_val & 3) || ((uintptr_t)out_idx & 3))
+    return TP_ERR_ALIGN;
+  if (M == 0) return TP_OK;
+  const LmWs w = lm_ws(cfg, L, M);
+  if (w.total > 0) {
+    if (!workspace) return TP_ERR_NULL;
+    if (!aligned16(workspace)) return TP_ERR_ALIGN;
+    if (ws_bytes < w.total) return TP_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t N = L.vocab_end - L.vocab_start, H = cfg->hidden;
+  if (N > 0) {
+    // logits GEMM whose epilogue leaves one candidate per row and N tile
+    GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), workspace, M, N, H, H, H,
+                  w.tiles_n, 0};
+    const hipError_t e = gemm_bf16(g, EPI_ARGMAX, nullptr, 0, s);
+    if (e != hipSuccess) return TP_ERR_LAUNCH;
+  }
+  return launched(argmax_candidates(workspace, M, w.tiles_n, L.vocab_start, out_val, out_idx, s));
+}
+
+int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, int64_t M, int32_t* out_idx,
+                      float* out_val_opt, void* stream) {
+  if (n_shards < 1 || M < 0) return TP_ERR_RANGE;
+  if (!vals || !idx || !out_idx) return TP_ERR_NULL;
+  if (((uintptr_t)vals & 3) || ((uintptr_t)idx & 3) || ((uintptr_t)out_idx & 3) || ((uintptr_t)out_val_opt & 3))
+    return TP_ERR_ALIGN;
+  if (M == 0) return TP_OK;
+  return launched(argmax_combine(vals, idx, n_shards, M, out_idx, out_val_opt, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

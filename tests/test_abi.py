@@ -170,3 +170,24 @@ def test_mlp_and_lm_head_validation():
     assert _status(tp.tp_lm_head, cv, A, 0, A, A, s) == OK
     assert _status(tp.tp_lm_head, cv, A, 4, MIS, A, s) == E_ALIGN
     assert _status(tp.tp_lm_head, tp.Cfg(hidden=256, tp_size=1), A, 4, A, A, s) == E_SHAPE
+
+
+def test_lm_head_argmax_and_combine_validation():
+    s = NullStream()
+    cv = tp.Cfg(hidden=256, vocab=1000, tp_size=4, tp_rank=3)
+    need = tp.tp_workspace_bytes(cv, tp.TP_OP_LM_ARGMAX, 5, 1)
+    assert need >= 5 * 8                                          # a candidate per row
+    ws = Fake(1 << 40, need, 1)
+    assert _status(tp.tp_lm_head_argmax, cv, A, 0, A, A, A, ws, s) == OK          # M = 0
+    assert _status(tp.tp_lm_head_argmax, cv, A, -1, A, A, A, ws, s) == E_RANGE
+    assert _status(tp.tp_lm_head_argmax, cv, A, 5, A, None, A, ws, s) == E_NULL
+    assert _status(tp.tp_lm_head_argmax, cv, A, 5, A, A, A, None, s) == E_NULL    # no workspace
+    assert _status(tp.tp_lm_head_argmax, cv, A, 5, A, A, A, Fake(1 << 40, need - 1, 1), s) == E_WS
+    assert _status(tp.tp_lm_head_argmax, cv, MIS, 5, A, A, A, ws, s) == E_ALIGN
+    assert _status(tp.tp_lm_head_argmax, tp.Cfg(hidden=256, vocab=1000, tp_size=4, dtype=tp.TP_F32),
+                   A, 5, A, A, A, ws, s) == E_DTYPE
+    assert _status(tp.tp_lm_head_argmax, tp.Cfg(hidden=256, tp_size=1), A, 5, A, A, A, ws, s) == E_SHAPE
+    assert _status(tp.tp_argmax_combine, A, A, 0, 5, A, None, s) == E_RANGE       # no shards
+    assert _status(tp.tp_argmax_combine, A, A, 2, 0, A, None, s) == OK            # M = 0
+    assert _status(tp.tp_argmax_combine, None, A, 2, 5, A, None, s) == E_NULL
+    assert _status(tp.tp_argmax_combine, A, Fake((1 << 40) + 2, 5), 2, 5, A, None, s) == E_ALIGN

@@ -479,3 +479,88 @@ def test_deterministic_reruns():
         outs.append([t.clone() for t in (q, a, part, kc, vc, h, mp)])
     for t1, t2 in zip(*outs):
         assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ greedy argmax
+
+def _argmax_case(V, H, n, M, wid, ties=False):
+    E = synth.embedding(wid, V, H)
+    x = synth.activations(wid, M, H)
+    if ties:
+        # copies of one row in several shards, and rows of x along it, so
+        # that the copies tie exactly at the maximum: the smallest id wins
+        k = V // 3
+        for j in (3, V // 2 + 1, V - 2):
+            E[j] = E[k]
+        for m in range(0, M, 4):
+            x[m] = (E[k].float() * 40.0).to(torch.bfloat16)
+    Eg, xg = E.to(DEV), x.to(DEV)
+    xc, Ec = synth.to_f64(x), synth.to_f64(E)
+    vals = torch.empty(n, M, dtype=torch.float32, device=DEV)
+    idx = torch.empty(n, M, dtype=torch.int32, device=DEV)
+    ov, oi = [], []
+    for r in range(n):
+        c = tp.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        L = tp.tp_local_dims(c)
+        shard = torch.empty(max(L.vocab_end - L.vocab_start, 1), H, dtype=torch.bfloat16, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_VOCAB, Eg, shard)
+        ws = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_LM_ARGMAX, M, 1), dtype=torch.uint8, device=DEV)
+        tp.tp_lm_head_argmax(c, xg, M, shard, vals[r], idx[r], ws)
+        v, i = O.lm_head_argmax(xc, Ec[L.vocab_start:L.vocab_end], L.vocab_start)
+        ov.append(v)
+        oi.append(i)
+    out_i = torch.empty(M, dtype=torch.int32, device=DEV)
+    out_v = torch.empty(M, dtype=torch.float32, device=DEV)
+    tp.tp_argmax_combine(vals, idx, n, M, out_i, out_v)
+    torch.cuda.synchronize()
+    ref_v, ref_i = O.argmax_combine(np.stack(ov), np.stack(oi))
+    return (vals.cpu().numpy(), idx.cpu().numpy(), out_v.cpu().numpy(), out_i.cpu().numpy(),
+            np.stack(ov), np.stack(oi), ref_v, ref_i, xc, Ec)
+
+
+def _check_argmax(gv, gi, rv, ri, xc, Ec):
+    """Token ids equal the oracle's, except where the oracle's top two logits
+    lie within one bf16 step of each other (then any of them is a correct
+    greedy token: fp32 and fp64 accumulation may round either way); values
+    are the bf16 logits of the chosen ids."""
+    for m in range(len(ri)):
+        if gi[m] == ri[m]:
+            assert gv[m] == rv[m], (m, gv[m], rv[m])
+            continue
+        logit = O.bf16(xc[m] @ Ec[gi[m]])
+        assert abs(logit - rv[m]) <= 2.0 ** -7 * abs(rv[m]), (m, gi[m], ri[m], logit, rv[m])
+
+
+def test_lm_head_argmax_decode_full_vocab():
+    """The 0.6B vocabulary (151936 over 2 ranks), 64 decode rows: per-rank
+    candidates and the combined greedy token against the oracle, and the
+    combined token against argmax over the concatenated oracle logits."""
+    w = synth.WORKLOADS[3]
+    gvr, gir, gv, gi, ov, oi, rv, ri, xc, Ec = _argmax_case(w["vocab"], w["hidden"], w["tp"], 64, 3)
+    for r in range(w["tp"]):
+        _check_argmax(gvr[r], gir[r], ov[r], oi[r], xc, Ec)
+    _check_argmax(gv, gi, rv, ri, xc, Ec)
+    full = O.bf16(xc @ Ec.T)
+    assert np.array_equal(ri, np.argmax(full, axis=1))
+
+
+@pytest.mark.parametrize("case", ["ragged-ties", "empty-shard"])
+def test_lm_head_argmax_ragged(case):
+    """Odd local vocab sizes (row stride not a multiple of 16 bytes), uneven
+    shards, planted exact ties across shards (the smallest id must win), and
+    an empty last shard that must never win."""
+    if case == "ragged-ties":
+        V, H, n, M = 1001, 520, 3, 37
+        out = _argmax_case(V, H, n, M, 13, ties=True)
+        assert (out[7][0::4] == 3).all()           # the oracle's winner is the first copy
+    else:
+        V, H, n, M = 5, 64, 4, 9
+        out = _argmax_case(V, H, n, M, 14)
+    gvr, gir, gv, gi, ov, oi, rv, ri, xc, Ec = out
+    for r in range(n):
+        if oi[r][0] < 0:
+            assert (gir[r] == -1).all() and np.isneginf(gvr[r]).all()
+        else:
+            _check_argmax(gvr[r], gir[r], ov[r], oi[r], xc, Ec)
+    _check_argmax(gv, gi, rv, ri, xc, Ec)
+    assert np.array_equal(gi, ri)
