@@ -326,6 +326,26 @@ def qkv_attn(c: Cfg, x, B, T, past, w_qkv_local, q_norm_w, k_norm_w, w_o_local,
 
 
 # --------------------------------------------------------------------------
+# residual add + RMSNorm after a row-parallel layer   ([TPS] Implementation,
+# TPTransformer.forward: x = x + attn(input_layernorm(x)), then
+# x = x + mlp(post_attention_layernorm(x)); each row-parallel output is the
+# all-reduce (sum over ranks) of the ranks' partials; "The cost of
+# communication": engines fuse that all-reduce with the following RMSNorm)
+# --------------------------------------------------------------------------
+
+def residual_rmsnorm(partials, residual, w, eps, store=bf16):
+    """partials: [n, M, H] (one per rank), residual: [M, H], w: [H].
+    h = store(residual + sum over ranks of partials)   the new residual stream
+    y = store(rms_norm(h, w, eps))                     the next layer's input
+    Returns (h, y)."""
+    total = np.asarray(residual, np.float64).copy()
+    for p in np.asarray(partials, np.float64):
+        total = total + p
+    h = store(total)
+    return h, store(rms_norm(h, np.asarray(w, np.float64), eps))
+
+
+# --------------------------------------------------------------------------
 # MLP shard   ([TPS] Implementation, TPMLP.forward)
 # --------------------------------------------------------------------------
 

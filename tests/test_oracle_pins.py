@@ -491,3 +491,31 @@ def test_argmax_combine_skips_empty_shards():
     x = O.bf16(_rand(84, (3, H)))
     v, i = _sharded_argmax(x, E, V, H, n)
     assert np.array_equal(i, np.argmax(O.bf16(x @ E.T), axis=1))
+
+
+# ------------------------------------------- residual + RMSNorm after the sum
+
+def test_residual_rmsnorm_matches_torch_sum_and_rms_norm():
+    """The fused step equals: sum the ranks' partials (the all-reduce), add
+    the residual, store bf16, then torch's rms_norm with the weight."""
+    n, M, H, eps = 3, 5, 96, 1e-6
+    P = O.bf16(_rand(90, (n, M, H)))
+    res = O.bf16(_rand(91, (M, H)))
+    w = O.bf16(np.random.default_rng(92).uniform(0.5, 1.5, H))
+    h, y = O.residual_rmsnorm(P, res, w, eps)
+    ht = (torch.from_numpy(res) + torch.from_numpy(P).sum(0)).to(torch.bfloat16)
+    yt = torch.nn.functional.rms_norm(ht.double(), (H,), torch.from_numpy(w), eps).to(torch.bfloat16)
+    np.testing.assert_array_equal(h, ht.double().numpy())
+    np.testing.assert_array_equal(y, yt.double().numpy())
+
+
+def test_residual_rmsnorm_special_cases():
+    """One rank with a zero partial is plain RMSNorm of the residual; with
+    unit weights every output row has unit RMS (before the bf16 store)."""
+    M, H, eps = 4, 64, 1e-6
+    res = O.bf16(_rand(93, (M, H)))
+    w = np.ones(H)
+    h, y = O.residual_rmsnorm(np.zeros((1, M, H)), res, w, eps, store=lambda v: np.asarray(v, np.float64))
+    np.testing.assert_array_equal(h, res)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(1)), 1.0, rtol=1e-6)
+    np.testing.assert_allclose(y, res / np.sqrt((res * res).mean(1, keepdims=True) + eps), rtol=1e-12)
