@@ -12,6 +12,8 @@ One step runs every row of the hot path once, on rank 0, in this order:
   decode  tp_qkv_attn (B sequences, 1 token, context c) + tp_mlp (B rows)
   decode_argmax  tp_lm_head_argmax over the B decode rows (this rank's greedy
           candidates over its vocab slice)
+  residual_norm  tp_residual_rmsnorm over the T prefill rows: the tp ranks'
+          partials summed into the residual stream, then the next RMSNorm
 HIP events on the launch stream bracket each phase.  `value` is the layer's
 prefill throughput (TFLOP/s of the prefill phase); decode GB/s, the lm_head
 TFLOP/s and the other phases are reported beside it.  Inputs are synthetic,
@@ -114,6 +116,11 @@ class Set:
         self.logits = torch.empty(n_ids, L.vocab_end - L.vocab_start, dtype=bf, device=dev)
         self.tok_val = torch.empty(B, dtype=torch.float32, device=dev)
         self.tok_idx = torch.empty(B, dtype=torch.int32, device=dev)
+        self.parts = src["parts"].clone()
+        self.resid = src["resid"].clone()
+        self.ln_w = src["ln_w"].clone()
+        self.h_res = torch.empty(T, H, dtype=bf, device=dev)
+        self.y_norm = torch.empty(T, H, dtype=bf, device=dev)
 
     def nbytes(self):
         import torch
@@ -153,6 +160,7 @@ def run_bench(args):
     vc[:, :, :ctx - 1] = pv[:, L.kv_head0:L.kv_head0 + L.lkv]
     del pv
     src["kc_dec"], src["vc_dec"] = kc.to(dev), vc.to(dev)
+    src["parts"], src["resid"], src["ln_w"] = (t.to(dev) for t in synth.norm_inputs(wid, n, T, H))
     sets = [Set(src, w, L, c, T, B, ctx, n_ids, V, H)]
     per_set = sets[0].nbytes()
     n_sets = max(2, -(-2 * MALL_BYTES // per_set) + 1)
@@ -168,7 +176,7 @@ def run_bench(args):
 
     kinds = ((tp.TP_W_Q, "q", "qkv"), (tp.TP_W_K, "k", "qkv"), (tp.TP_W_V, "v", "qkv"), (tp.TP_W_O, "o", "o"),
              (tp.TP_W_GATE, "gate", "gu"), (tp.TP_W_UP, "up", "gu"), (tp.TP_W_DOWN, "down", "down"))
-    phases = ["shard", "embed", "prefill", "lm_head", "decode", "decode_argmax"]
+    phases = ["shard", "embed", "prefill", "lm_head", "decode", "decode_argmax", "residual_norm"]
 
     def step(s: Set, ev=None):
         rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
@@ -191,6 +199,8 @@ def run_bench(args):
         rec(5)
         tp.tp_lm_head_argmax(c, s.x_dec, B, s.vocab, s.tok_val, s.tok_idx, ws_lm)
         rec(6)
+        tp.tp_residual_rmsnorm(c, s.parts, n, T, s.resid, s.ln_w, s.h_res, s.y_norm)
+        rec(7)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
@@ -219,6 +229,8 @@ def run_bench(args):
     # greedy decode head: the vocab slice and the decode rows are read once;
     # one (value, id) pair per row is written
     argmax_bytes = 2 * nv * H + 2 * B * H + 8 * B
+    # residual + RMSNorm: n partials and the residual read, h and y written
+    norm_bytes = 2 * (n + 1) * T * H + 2 * 2 * T * H + 2 * H
     shard_bytes = 2 * 2 * (L.n_qkv * H + H * L.lq * 128 + 2 * L.li * H + H * L.li + nv * H)
 
     prefill_tflops = prefill_flops / ph["prefill"] / 1e12
@@ -250,6 +262,8 @@ def run_bench(args):
         "lm_head_pct_mfma_peak": round(100 * lm_tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "decode_argmax_GBps": round(argmax_bytes / ph["decode_argmax"] / 1e9, 1),
         "decode_argmax_pct_hbm_peak": round(100 * argmax_bytes / ph["decode_argmax"] / 1e9 / HBM_PEAK_GBPS, 2),
+        "residual_norm_GBps": round(norm_bytes / ph["residual_norm"] / 1e9, 1),
+        "residual_norm_pct_hbm_peak": round(100 * norm_bytes / ph["residual_norm"] / 1e9 / HBM_PEAK_GBPS, 2),
         "embed_GBps": round(emb_bytes / ph["embed"] / 1e9, 1),
         "shard_GBps": round(shard_bytes / ph["shard"] / 1e9, 1),
         "phase_us": {p: round(v * 1e6, 2) for p, v in ph.items()},

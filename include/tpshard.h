@@ -231,6 +231,21 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* v
 int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, int64_t M,
                       int32_t* out_idx, float* out_val_opt, void* stream);
 
+/* tp_residual_rmsnorm -- the replicated step after a row-parallel layer,
+ * with its all-reduce ([TPS] "Implementation", TPTransformer.forward: the
+ * residual add and the next RMSNorm; "The cost of communication": fusing the
+ * all-reduce with the following RMSNorm):
+ *   h = bf16(residual + sum_{r < n_partials} partials[r])   (fp32 sum in rank order)
+ *   y = bf16(h / sqrt(mean(h^2) + rms_eps) * norm_w)
+ * partials: bf16 [n_partials, M, H] (the ranks' tp_qkv_attn / tp_mlp
+ * out_partial, stacked: on one GPU this stands in for the all-reduce);
+ * residual, h_out, y_out: bf16 [M, H]; norm_w: bf16 [H].  h_out may be the
+ * residual buffer (in-place update of the residual stream); y_out must not
+ * overlap the inputs.  Requires TP_BF16 (TP_ERR_DTYPE), H % 8 == 0 and
+ * H <= 8192 (TP_ERR_SHAPE), n_partials >= 1 (TP_ERR_RANGE).  M = 0: no-op. */
+int tp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int32_t n_partials, int64_t M,
+                        const void* residual, const void* norm_w, void* h_out, void* y_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,7 +4,8 @@ method's arithmetic.  bf16 inputs are produced by torch's own fp32->bf16
 conversion so that both sides see identical bits.
 
 Tensor ids (second seed word): 0 x, 1 q, 2 k, 3 v, 4 o, 5 gate, 6 up, 7 down,
-8 q_norm, 9 k_norm, 10 prior K cache, 11 prior V cache, 12 ids, 13 embedding.
+8 q_norm, 9 k_norm, 10 prior K cache, 11 prior V cache, 12 ids, 13 embedding,
+14 row-parallel partials, 15 residual stream, 16 layer-norm weight.
 Generator: numpy.random.default_rng([workload_id, tensor_id]).
 """
 from __future__ import annotations
@@ -12,7 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-T_X, T_Q, T_K, T_V, T_O, T_GATE, T_UP, T_DOWN, T_QN, T_KN, T_KC, T_VC, T_IDS, T_EMB = range(14)
+(T_X, T_Q, T_K, T_V, T_O, T_GATE, T_UP, T_DOWN, T_QN, T_KN, T_KC, T_VC, T_IDS, T_EMB,
+ T_PART, T_RES, T_LNW) = range(17)
 
 # The five workloads: model shapes (Qwen3-0.6B / Qwen3-32B) and per-rank sizes.
 WORKLOADS = {
@@ -83,6 +85,14 @@ def prior_cache(wid: int, tid: int, B: int, n_kv_heads: int, S: int, d: int) -> 
     """Cache contents for positions already written, per GLOBAL kv head:
     [B, n_kv_heads, S, d] ~ N(0,1); a rank copies its own heads out of it."""
     return normal(wid, tid, (B, n_kv_heads, S, d), 1.0)
+
+
+def norm_inputs(wid: int, n: int, rows: int, hidden: int, dtype=torch.bfloat16):
+    """Inputs of the residual add + RMSNorm after a row-parallel layer:
+    n stacked rank partials [n, rows, hidden] ~ N(0, 0.5), the residual
+    stream [rows, hidden] ~ N(0, 1) and the norm weight ~ U(0.5, 1.5)."""
+    return (normal(wid, T_PART, (n, rows, hidden), 0.5, dtype), normal(wid, T_RES, (rows, hidden), 1.0, dtype),
+            uniform(wid, T_LNW, (hidden,), 0.5, 1.5, dtype))
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -21,7 +21,8 @@ TP_W_Q, TP_W_K, TP_W_V, TP_W_O, TP_W_GATE, TP_W_UP, TP_W_DOWN, TP_W_VOCAB = rang
 TP_OP_ATTN, TP_OP_MLP, TP_OP_LM_ARGMAX = 0, 1, 2
 
 EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_shard_weights", "tp_embed_vocab",
-           "tp_qkv_attn", "tp_mlp", "tp_lm_head", "tp_lm_head_argmax", "tp_argmax_combine")
+           "tp_qkv_attn", "tp_mlp", "tp_lm_head", "tp_lm_head_argmax", "tp_argmax_combine",
+           "tp_residual_rmsnorm")
 
 
 class TpError(RuntimeError):
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
         L.tp_lm_head.argtypes = [C, P, I64, P, P, P]
         L.tp_lm_head_argmax.argtypes = [C, P, I64, P, P, P, P, SZ, P]
         L.tp_argmax_combine.argtypes = [P, P, I32, I64, P, P, P]
+        L.tp_residual_rmsnorm.argtypes = [C, P, I32, I64, P, P, P, P, P]
         for name in EXPORTS:
             if name != "tp_status_str":
                 getattr(L, name).restype = ctypes.c_int
@@ -179,3 +181,8 @@ def tp_lm_head_argmax(cfg: Cfg, x, M: int, vocab_local, out_val, out_idx, worksp
 
 def tp_argmax_combine(vals, idx, n_shards: int, M: int, out_idx, out_val=None, stream=None):
     _check(lib().tp_argmax_combine(_ptr(vals), _ptr(idx), n_shards, M, _ptr(out_idx), _ptr(out_val), _stream(stream)))
+
+
+def tp_residual_rmsnorm(cfg: Cfg, partials, n_partials: int, M: int, residual, norm_w, h_out, y_out, stream=None):
+    _check(lib().tp_residual_rmsnorm(ctypes.byref(cfg.c()), _ptr(partials), n_partials, M, _ptr(residual),
+                                     _ptr(norm_w), _ptr(h_out), _ptr(y_out), _stream(stream)))

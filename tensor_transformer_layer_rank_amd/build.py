@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libtpshard.so")
 ARCH = "gfx950"
 
 SOURCES = ["tpshard.cpp", "copy_kernels.hip", "gemm.hip", "attn_prefill.hip",
-           "attn_flash.hip", "lm_argmax.hip"]
+           "attn_flash.hip", "lm_argmax.hip", "norm.hip"]
 
 
 def hipcc() -> str:

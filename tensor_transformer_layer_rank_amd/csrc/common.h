@@ -106,4 +106,10 @@ hipError_t argmax_candidates(const void* cand, int64_t M, int64_t n, int64_t idx
 hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, int64_t M, int32_t* out_idx,
                           float* out_val, hipStream_t s);
 
+// --- residual + RMSNorm over summed row-parallel partials -----------------
+// h = bf16(residual + sum_r partials[r]), y = bf16(rms_norm(h) * w); one row
+// per workgroup, H % 8 == 0 and H <= 8192; h_out may alias residual.
+hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t M, int H, const bf16* residual, const bf16* w,
+                            float eps, bf16* h_out, bf16* y_out, hipStream_t s);
+
 }  // namespace tps

@@ -363,4 +363,22 @@ int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, i
   return launched(argmax_combine(vals, idx, n_shards, M, out_idx, out_val_opt, static_cast<hipStream_t>(stream)));
 }
 
+int tp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int32_t n_partials, int64_t M, const void* residual,
+                        const void* norm_w, void* h_out, void* y_out, void* stream) {
+  int st = check_cfg(cfg, nullptr);
+  if (st) return st;
+  if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (cfg->hidden % 8 || cfg->hidden > 8192) return TP_ERR_SHAPE;
+  if (n_partials < 1 || M < 0) return TP_ERR_RANGE;
+  if (!partials || !residual || !norm_w || !h_out || !y_out) return TP_ERR_NULL;
+  const void* ptrs[] = {partials, residual, norm_w, h_out, y_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TP_ERR_ALIGN;
+  if (M == 0) return TP_OK;
+  return launched(residual_rmsnorm(static_cast<const bf16*>(partials), n_partials, M, cfg->hidden,
+                                   static_cast<const bf16*>(residual), static_cast<const bf16*>(norm_w),
+                                   cfg->rms_eps, static_cast<bf16*>(h_out), static_cast<bf16*>(y_out),
+                                   static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

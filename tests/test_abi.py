@@ -191,3 +191,18 @@ def test_lm_head_argmax_and_combine_validation():
     assert _status(tp.tp_argmax_combine, A, A, 2, 0, A, None, s) == OK            # M = 0
     assert _status(tp.tp_argmax_combine, None, A, 2, 5, A, None, s) == E_NULL
     assert _status(tp.tp_argmax_combine, A, Fake((1 << 40) + 2, 5), 2, 5, A, None, s) == E_ALIGN
+
+
+def test_residual_rmsnorm_validation():
+    s = NullStream()
+    c = tp.Cfg(hidden=256, tp_size=2)
+    assert _status(tp.tp_residual_rmsnorm, c, A, 2, 0, A, A, A, A, s) == OK             # M = 0
+    assert _status(tp.tp_residual_rmsnorm, c, A, 2, -1, A, A, A, A, s) == E_RANGE
+    assert _status(tp.tp_residual_rmsnorm, c, A, 0, 5, A, A, A, A, s) == E_RANGE        # no partials
+    assert _status(tp.tp_residual_rmsnorm, c, A, 2, 5, None, A, A, A, s) == E_NULL
+    assert _status(tp.tp_residual_rmsnorm, c, A, 2, 5, A, A, A, None, s) == E_NULL
+    assert _status(tp.tp_residual_rmsnorm, c, A, 2, 5, A, A, MIS, A, s) == E_ALIGN
+    assert _status(tp.tp_residual_rmsnorm, tp.Cfg(hidden=250, tp_size=2), A, 2, 5, A, A, A, A, s) == E_SHAPE
+    assert _status(tp.tp_residual_rmsnorm, tp.Cfg(hidden=8200, tp_size=2), A, 2, 5, A, A, A, A, s) == E_SHAPE
+    assert _status(tp.tp_residual_rmsnorm, tp.Cfg(hidden=256, tp_size=2, dtype=tp.TP_F32),
+                   A, 2, 5, A, A, A, A, s) == E_DTYPE

@@ -564,3 +564,73 @@ def test_lm_head_argmax_ragged(case):
             _check_argmax(gvr[r], gir[r], ov[r], oi[r], xc, Ec)
     _check_argmax(gv, gi, rv, ri, xc, Ec)
     assert np.array_equal(gi, ri)
+
+
+def bf16_ulp(a):
+    """One bf16 unit in the last place at |a| (fp32 spacing scaled by 2^16)."""
+    a = np.abs(np.asarray(a, np.float64)).astype(np.float32)
+    return np.spacing(np.maximum(a, np.float32(2.0 ** -100))).astype(np.float64) * 65536.0
+
+
+NORM_CASES = {
+    # name: (workload id, partials n, rows M, hidden H, rows the oracle checks or None for all)
+    "0.6b-tp2-prefill": (2, 2, 2048, 1024, None),
+    "32b-tp16-decode": (5, 16, 256, 5120, None),
+    "32b-tp2-prefill-sampled": (4, 2, 4096, 5120, [0, 1, 2, 3, 511, 2048, 3333, 4092, 4093, 4094, 4095]),
+    "ragged-h520": (20, 3, 7, 520, None),
+    "two-wave-rows-h2056": (24, 5, 11, 2056, None),
+    "max-h8192": (21, 1, 5, 8192, None),
+    "h8": (22, 2, 9, 8, None),
+}
+
+
+def _run_norm(wid, n, M, H, inplace=False):
+    P, R, Wn = synth.norm_inputs(wid, n, M, H)
+    c = tp.Cfg(hidden=H, tp_size=n)
+    Pg, Rg, Wg = P.to(DEV), R.to(DEV), Wn.to(DEV)
+    hg = Rg if inplace else torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    yg = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tp.tp_residual_rmsnorm(c, Pg, n, M, Rg, Wg, hg, yg)
+    torch.cuda.synchronize()
+    return P, R, Wn, c, hg, yg
+
+
+def _check_norm(P, R, Wn, eps, hg, yg, rows):
+    Pc, Rc, Wc = synth.to_f64(P), synth.to_f64(R), synth.to_f64(Wn)
+    if rows is not None:
+        Pc, Rc = Pc[:, rows], Rc[rows]
+        hg, yg = hg[rows], yg[rows]
+    h_ref, y_ref = O.residual_rmsnorm(Pc, Rc, Wc, eps)
+    h, y = f64(hg), f64(yg)
+    assert relerr(h, h_ref) <= TOL_BF16 and relerr(y, y_ref) <= TOL_BF16
+    # fp32 against fp64 sums of bf16 terms: at most one rounding step apart
+    assert (np.abs(h - h_ref) <= bf16_ulp(np.maximum(np.abs(h), np.abs(h_ref)))).all()
+    assert (np.abs(y - y_ref) <= 2 * bf16_ulp(np.maximum(np.abs(y), np.abs(y_ref)))).all()
+
+
+@pytest.mark.parametrize("case", list(NORM_CASES))
+def test_residual_rmsnorm(case):
+    """Residual add of the summed row-parallel partials and the next RMSNorm
+    against the oracle: the 0.6B tp2 prefill rows and the 32B tp16 decode
+    batch element by element, the 32B tp2 prefill on sampled rows (first,
+    last, ragged last workgroup), a hidden size that leaves one lane of a
+    second chunk (520), two-wave rows with a partial count that is not a
+    multiple of the load group (2056, 5 partials), the largest supported
+    hidden size and the smallest."""
+    wid, n, M, H, rows = NORM_CASES[case]
+    P, R, Wn, c, hg, yg = _run_norm(wid, n, M, H)
+    _check_norm(P, R, Wn, c.rms_eps, hg, yg, rows)
+
+
+def test_residual_rmsnorm_inplace_and_empty():
+    """The residual buffer updated in place gives the same h and y; M = 0
+    writes nothing."""
+    P, R, Wn, c, hg, yg = _run_norm(23, 2, 33, 1024, inplace=True)
+    _check_norm(P, R, Wn, c.rms_eps, hg, yg, None)
+    _, _, _, c, h0, y0 = _run_norm(23, 2, 33, 1024)
+    assert torch.equal(h0.view(torch.int16), hg.view(torch.int16))
+    assert torch.equal(y0.view(torch.int16), yg.view(torch.int16))
+    y = torch.full((4, 1024), 7.0, dtype=torch.bfloat16, device=DEV)
+    tp.tp_residual_rmsnorm(c, y, 2, 0, y, y[0], y, y)
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
