@@ -29,6 +29,8 @@ Readings where the pages are silent (each also listed in the design notes):
   * Attention scale is 1/sqrt(head_dim) (the SDPA default the pages rely on).
   * Merge order is qkv = [q; k; v] and gate_up = [gate; up] along dim 0.
   * A vocab shard whose start passes the vocab size is empty (start clamped).
+  * Sequence parallelism cuts the tokens like the vocab: ceil(M / tp) rows per
+    rank, in rank order, the last slices shorter or empty.
 """
 from __future__ import annotations
 
@@ -342,6 +344,51 @@ def residual_rmsnorm(partials, residual, w, eps, store=bf16):
     for p in np.asarray(partials, np.float64):
         total = total + p
     h = store(total)
+    return h, store(rms_norm(h, np.asarray(w, np.float64), eps))
+
+
+# --------------------------------------------------------------------------
+# sequence-parallel variant   ([TPS] "Exercises", the sequence-parallelism
+# exercise: the all-reduce after o_proj / down becomes a reduce-scatter over
+# tokens, so that each rank holds the full sum for its 1/tp of the tokens; the
+# residual add and RMSNorm run on those rows only; an all-gather brings every
+# token back before the next column-split layer)
+# --------------------------------------------------------------------------
+
+def sp_rows(M, n, r):
+    """Rank r's token slice [start, end) of M rows: contiguous blocks of
+    ceil(M / n) rows in rank order, the last ones shorter or empty (the pages
+    do not say how a token count that tp does not divide is cut; this is the
+    rule the vocab split uses)."""
+    if not (0 <= r < n):
+        raise ValueError("rank out of range")
+    per = -(-M // n) if M else 0
+    return min(r * per, M), min((r + 1) * per, M)
+
+
+def reduce_scatter(partials, n, r):
+    """Rank r's rows of the sum over ranks of the partials [n, M, H]."""
+    partials = np.asarray(partials, np.float64)
+    s, e = sp_rows(partials.shape[1], n, r)
+    total = np.zeros((e - s,) + partials.shape[2:], np.float64)
+    for p in partials:
+        total = total + p[s:e]
+    return total
+
+
+def all_gather(slices):
+    """The ranks' token slices, in rank order, back to all tokens."""
+    return np.concatenate([np.asarray(t, np.float64) for t in slices], axis=0)
+
+
+def sp_residual_rmsnorm(partials, residual_slice, w, eps, r, store=bf16):
+    """partials: [n, M, H], every rank's partial over all M tokens (n = tp);
+    residual_slice: rank r's rows of the residual stream, [end - start, H].
+    h = store(residual_slice + reduce_scatter(partials))   this rank's rows
+    y = store(rms_norm(h, w, eps))                          this rank's rows
+    Returns (h, y); all_gather of every rank's y is the next layer's input."""
+    partials = np.asarray(partials, np.float64)
+    h = store(np.asarray(residual_slice, np.float64) + reduce_scatter(partials, partials.shape[0], r))
     return h, store(rms_norm(h, np.asarray(w, np.float64), eps))
 
 

@@ -519,3 +519,55 @@ def test_residual_rmsnorm_special_cases():
     np.testing.assert_array_equal(h, res)
     np.testing.assert_allclose(np.sqrt((y * y).mean(1)), 1.0, rtol=1e-6)
     np.testing.assert_allclose(y, res / np.sqrt((res * res).mean(1, keepdims=True) + eps), rtol=1e-12)
+
+
+@pytest.mark.parametrize("M,n", [(0, 2), (1, 2), (7, 2), (8, 4), (9, 4), (5, 8), (4096, 2), (1023, 16)])
+def test_sp_rows_match_torch_chunk(M, n):
+    """The token slices are torch.chunk's pieces in rank order (ranks past the
+    pieces torch returns get empty slices): contiguous, disjoint, covering."""
+    rows = torch.arange(M)
+    pieces = torch.chunk(rows, n) if M else ()
+    end = 0
+    for r in range(n):
+        s, e = O.sp_rows(M, n, r)
+        assert s == end and s <= e
+        got = rows[s:e]
+        want = pieces[r] if r < len(pieces) else rows[:0]
+        assert torch.equal(got, want), (M, n, r)
+        end = e
+    assert end == M
+
+
+def test_reduce_scatter_then_all_gather_is_all_reduce():
+    """Reduce-scatter + all-gather equals the all-reduce (torch's sum over
+    ranks), for a token count that tp does not divide."""
+    n, M, H = 3, 10, 24
+    P = _rand(94, (n, M, H))
+    got = O.all_gather([O.reduce_scatter(P, n, r) for r in range(n)])
+    np.testing.assert_array_equal(got, torch.from_numpy(P).sum(0).numpy())
+    s, e = O.sp_rows(M, n, 1)
+    assert O.reduce_scatter(P, n, 1).shape == (e - s, H)
+
+
+@pytest.mark.parametrize("M,n", [(6, 2), (7, 4), (3, 4)])
+def test_sp_residual_rmsnorm_gathers_to_torch(M, n):
+    """Every rank normalises only its own rows; the gathered result equals
+    torch's sum + rms_norm over all tokens (and the non-sequence-parallel
+    fused step), including ranks that own no token."""
+    H, eps = 64, 1e-6
+    P = O.bf16(_rand(95, (n, M, H)))
+    res = O.bf16(_rand(96, (M, H)))
+    w = O.bf16(np.random.default_rng(97).uniform(0.5, 1.5, H))
+    hs, ys = [], []
+    for r in range(n):
+        s, e = O.sp_rows(M, n, r)
+        h, y = O.sp_residual_rmsnorm(P, res[s:e], w, eps, r)
+        assert h.shape == y.shape == (e - s, H)
+        hs.append(h)
+        ys.append(y)
+    ht = (torch.from_numpy(res) + torch.from_numpy(P).sum(0)).to(torch.bfloat16)
+    yt = torch.nn.functional.rms_norm(ht.double(), (H,), torch.from_numpy(w), eps).to(torch.bfloat16)
+    np.testing.assert_array_equal(O.all_gather(hs), ht.double().numpy())
+    np.testing.assert_array_equal(O.all_gather(ys), yt.double().numpy())
+    h_full, y_full = O.residual_rmsnorm(P, res, w, eps)
+    np.testing.assert_array_equal(O.all_gather(ys), y_full)
