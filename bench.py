@@ -14,6 +14,8 @@ One step runs every row of the hot path once, on rank 0, in this order:
           candidates over its vocab slice)
   residual_norm  tp_residual_rmsnorm over the T prefill rows: the tp ranks'
           partials summed into the residual stream, then the next RMSNorm
+  sp_norm tp_sp_residual_rmsnorm, the sequence-parallel form: rank 0's
+          ceil(T / tp) token rows only, written into the gathered output
 HIP events on the launch stream bracket each phase.  `value` is the layer's
 prefill throughput (TFLOP/s of the prefill phase); decode GB/s, the lm_head
 TFLOP/s and the other phases are reported beside it.  Inputs are synthetic,
@@ -176,7 +178,8 @@ def run_bench(args):
 
     kinds = ((tp.TP_W_Q, "q", "qkv"), (tp.TP_W_K, "k", "qkv"), (tp.TP_W_V, "v", "qkv"), (tp.TP_W_O, "o", "o"),
              (tp.TP_W_GATE, "gate", "gu"), (tp.TP_W_UP, "up", "gu"), (tp.TP_W_DOWN, "down", "down"))
-    phases = ["shard", "embed", "prefill", "lm_head", "decode", "decode_argmax", "residual_norm"]
+    phases = ["shard", "embed", "prefill", "lm_head", "decode", "decode_argmax", "residual_norm", "sp_norm"]
+    sp0, sp1 = tp.tp_sp_rows(c, T)
 
     def step(s: Set, ev=None):
         rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
@@ -201,6 +204,8 @@ def run_bench(args):
         rec(6)
         tp.tp_residual_rmsnorm(c, s.parts, n, T, s.resid, s.ln_w, s.h_res, s.y_norm)
         rec(7)
+        tp.tp_sp_residual_rmsnorm(c, s.parts, T, s.resid[sp0:sp1], s.ln_w, s.h_res[sp0:sp1], s.y_norm)
+        rec(8)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
@@ -231,6 +236,8 @@ def run_bench(args):
     argmax_bytes = 2 * nv * H + 2 * B * H + 8 * B
     # residual + RMSNorm: n partials and the residual read, h and y written
     norm_bytes = 2 * (n + 1) * T * H + 2 * 2 * T * H + 2 * H
+    sp_rows = sp1 - sp0
+    sp_bytes = 2 * (n + 1) * sp_rows * H + 2 * 2 * sp_rows * H + 2 * H
     shard_bytes = 2 * 2 * (L.n_qkv * H + H * L.lq * 128 + 2 * L.li * H + H * L.li + nv * H)
 
     prefill_tflops = prefill_flops / ph["prefill"] / 1e12
@@ -264,6 +271,8 @@ def run_bench(args):
         "decode_argmax_pct_hbm_peak": round(100 * argmax_bytes / ph["decode_argmax"] / 1e9 / HBM_PEAK_GBPS, 2),
         "residual_norm_GBps": round(norm_bytes / ph["residual_norm"] / 1e9, 1),
         "residual_norm_pct_hbm_peak": round(100 * norm_bytes / ph["residual_norm"] / 1e9 / HBM_PEAK_GBPS, 2),
+        "sp_norm_GBps": round(sp_bytes / ph["sp_norm"] / 1e9, 1),
+        "sp_norm_pct_hbm_peak": round(100 * sp_bytes / ph["sp_norm"] / 1e9 / HBM_PEAK_GBPS, 2),
         "embed_GBps": round(emb_bytes / ph["embed"] / 1e9, 1),
         "shard_GBps": round(shard_bytes / ph["shard"] / 1e9, 1),
         "phase_us": {p: round(v * 1e6, 2) for p, v in ph.items()},

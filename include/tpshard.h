@@ -246,6 +246,36 @@ int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, i
 int tp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int32_t n_partials, int64_t M,
                         const void* residual, const void* norm_w, void* h_out, void* y_out, void* stream);
 
+/* tp_sp_rows -- host only, no HIP call: rank tp_rank's token slice
+ * [*row0, *row1) of M tokens under sequence parallelism ([TPS] "Exercises",
+ * sequence parallelism: each rank keeps the full sum for 1/tp of the
+ * tokens).  Contiguous blocks of ceil(M / tp_size) rows in rank order; the
+ * last slices may be shorter or empty (the vocab split's rule; the pages do
+ * not fix a token count that tp does not divide).  M < 0: TP_ERR_RANGE. */
+int tp_sp_rows(const tp_cfg* cfg, int64_t M, int64_t* row0, int64_t* row1);
+
+/* tp_sp_residual_rmsnorm -- the sequence-parallel form of
+ * tp_residual_rmsnorm ([TPS] "Exercises", sequence parallelism: the
+ * all-reduce after o_proj / down splits into a reduce-scatter over tokens,
+ * the residual add and RMSNorm run on the rank's own tokens, and an
+ * all-gather restores all tokens before the next column-split layer).  With
+ * [row0, row1) = tp_sp_rows(cfg, M) and S = row1 - row0:
+ *   reduce-scatter: rows [row0, row1) of sum_{r < tp_size} partials[r]
+ *   h_slice = bf16(residual_slice + that)              (fp32, rank order)
+ *   y       = bf16(h_slice / sqrt(mean(h^2) + rms_eps) * norm_w)
+ *   all-gather: y is written to rows [row0, row1) of y_gathered.
+ * partials: bf16 [tp_size, M, H], every rank's partial over all M tokens
+ * (on one GPU this stands in for the reduce-scatter's inputs);
+ * residual_slice, h_slice_out: bf16 [S, H] (this rank's rows of the residual
+ * stream; h_slice_out may be residual_slice); norm_w: bf16 [H]; y_gathered:
+ * bf16 [M, H], of which only this rank's rows are written (every rank
+ * writing its rows into one buffer is the all-gather).  Requires TP_BF16
+ * (TP_ERR_DTYPE), H % 8 == 0 and H <= 8192 (TP_ERR_SHAPE).  A rank whose
+ * slice is empty returns TP_OK without reading or writing anything (its
+ * pointers may then be NULL). */
+int tp_sp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int64_t M, const void* residual_slice,
+                           const void* norm_w, void* h_slice_out, void* y_gathered, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ TP_OP_ATTN, TP_OP_MLP, TP_OP_LM_ARGMAX = 0, 1, 2
 
 EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_shard_weights", "tp_embed_vocab",
            "tp_qkv_attn", "tp_mlp", "tp_lm_head", "tp_lm_head_argmax", "tp_argmax_combine",
-           "tp_residual_rmsnorm")
+           "tp_residual_rmsnorm", "tp_sp_rows", "tp_sp_residual_rmsnorm")
 
 
 class TpError(RuntimeError):
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.tp_lm_head_argmax.argtypes = [C, P, I64, P, P, P, P, SZ, P]
         L.tp_argmax_combine.argtypes = [P, P, I32, I64, P, P, P]
         L.tp_residual_rmsnorm.argtypes = [C, P, I32, I64, P, P, P, P, P]
+        L.tp_sp_rows.argtypes = [C, I64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        L.tp_sp_residual_rmsnorm.argtypes = [C, P, I64, P, P, P, P, P]
         for name in EXPORTS:
             if name != "tp_status_str":
                 getattr(L, name).restype = ctypes.c_int
@@ -186,3 +188,16 @@ def tp_argmax_combine(vals, idx, n_shards: int, M: int, out_idx, out_val=None, s
 def tp_residual_rmsnorm(cfg: Cfg, partials, n_partials: int, M: int, residual, norm_w, h_out, y_out, stream=None):
     _check(lib().tp_residual_rmsnorm(ctypes.byref(cfg.c()), _ptr(partials), n_partials, M, _ptr(residual),
                                      _ptr(norm_w), _ptr(h_out), _ptr(y_out), _stream(stream)))
+
+
+def tp_sp_rows(cfg: Cfg, M: int):
+    """Rank cfg.tp_rank's token slice (row0, row1) of M tokens."""
+    r0, r1 = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().tp_sp_rows(ctypes.byref(cfg.c()), M, ctypes.byref(r0), ctypes.byref(r1)))
+    return r0.value, r1.value
+
+
+def tp_sp_residual_rmsnorm(cfg: Cfg, partials, M: int, residual_slice, norm_w, h_slice_out, y_gathered,
+                           stream=None):
+    _check(lib().tp_sp_residual_rmsnorm(ctypes.byref(cfg.c()), _ptr(partials), M, _ptr(residual_slice),
+                                        _ptr(norm_w), _ptr(h_slice_out), _ptr(y_gathered), _stream(stream)))

@@ -8,6 +8,8 @@
 
 namespace tps {
 
+constexpr int kCUs = 256;   // compute units (8 XCDs x 32)
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -107,9 +109,11 @@ hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, i
                           float* out_val, hipStream_t s);
 
 // --- residual + RMSNorm over summed row-parallel partials -----------------
-// h = bf16(residual + sum_r partials[r]), y = bf16(rms_norm(h) * w); one row
-// per workgroup, H % 8 == 0 and H <= 8192; h_out may alias residual.
-hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t M, int H, const bf16* residual, const bf16* w,
-                            float eps, bf16* h_out, bf16* y_out, hipStream_t s);
+// h = bf16(residual + sum_r partials[r * plane]), y = bf16(rms_norm(h) * w)
+// over M rows of H; H % 8 == 0 and H <= 8192; h_out may alias residual.
+hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
+                            const bf16* w, float eps, bf16* h_out, bf16* y_out, hipStream_t s);
+// threads that residual_rmsnorm gives one row of M x H (64 .. 1024)
+int norm_threads_per_row(int64_t M, int H);
 
 }  // namespace tps

@@ -21,7 +21,6 @@ namespace tps {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kCUs = 256;
 
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   const int xcd = bid % kXcds, idx = bid / kXcds;

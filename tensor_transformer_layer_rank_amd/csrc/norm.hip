@@ -8,9 +8,12 @@
 //   h = bf16(residual + sum_r partial_r)      the new residual stream
 //   y = bf16(h / sqrt(mean(h^2) + eps) * w)   the next layer's normed input
 //
-// On one GPU the ranks' partials arrive stacked [n, M, H] and are summed
-// here in rank order (fp32, residual first), in the same pass as the add and
-// the norm.  The threads of a row keep it in registers between the sum and
+// On one GPU the ranks' partials arrive stacked (partial r of row m at
+// partials + r * plane + m * H) and are summed here in rank order (fp32,
+// residual first), in the same pass as the add and the norm.  The
+// sequence-parallel form ("Exercises", sequence parallelism) is the same pass
+// over the rank's token slice: plane stays the full M * H, the row pointers
+// start at the slice.  The threads of a row keep it in registers between the sum and
 // the scaling: every input byte is read once and each output written once.
 #include "common.h"
 
@@ -18,30 +21,30 @@ namespace tps {
 
 namespace {
 
-constexpr int kNormThreads = 256;
-constexpr int kNormGroup = 4;   // partials whose loads are in flight together
+// TPR threads per row (one wave up to a 1024-thread workgroup), NC 16-byte
+// chunks per thread: H <= TPR * NC * 8.  A workgroup holds max(TPR, 256)
+// threads, so up to four rows.  The partials are read G at a time, all G
+// loads in flight together; G shrinks as the chunks per thread grow so that
+// the loads fit in registers.
+template <int NC>
+constexpr int norm_group() { return NC == 1 ? 16 : NC == 2 ? 8 : 4; }
 
-// TPR threads (one to four waves) per row, NC 16-byte chunks per thread:
-// H <= TPR * NC * 8.  Wide rows spread over more waves so that a launch has
-// enough loads in flight; the partials are read kNormGroup at a time.
 template <int TPR, int NC>
-__global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(const bf16* __restrict__ partials, int n,
-                                                                        int64_t M, int H, const bf16* residual,
-                                                                        const bf16* __restrict__ w, float eps,
-                                                                        bf16* h_out, bf16* __restrict__ y_out) {
-  constexpr int ROWS = kNormThreads / TPR;
+__global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel(
+    const bf16* __restrict__ partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
+    const bf16* __restrict__ w, float eps, bf16* h_out, bf16* __restrict__ y_out) {
+  constexpr int BLOCK = TPR > 256 ? TPR : 256, ROWS = BLOCK / TPR, G = norm_group<NC>();
   const int t = threadIdx.x % TPR;
   const int64_t m = (int64_t)blockIdx.x * ROWS + threadIdx.x / TPR;
   const bool live = m < M;
   const int nc = H / 8;
   const int64_t row = (live ? m : 0) * H;
-  const int64_t plane = M * H;
   bool on[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) on[k] = live && t + k * TPR < nc;
   // residual, norm weight and the first group of partials are all
   // requested before the first use of any of them
-  bf16x8 rv[NC], wv[NC], v[kNormGroup][NC];
+  bf16x8 rv[NC], wv[NC], v[G][NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k)
     if (on[k]) {
@@ -49,9 +52,9 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(const bf
       wv[k] = *reinterpret_cast<const bf16x8*>(w + (int64_t)(t + k * TPR) * 8);
     }
   float acc[NC][8];
-  for (int r0 = 0; r0 < n; r0 += kNormGroup) {
+  for (int r0 = 0; r0 < n; r0 += G) {
 #pragma unroll
-    for (int g = 0; g < kNormGroup; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int k = 0; k < NC; ++k)
         if (r0 + g < n && on[k])
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(const bf
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = on[k] ? bf2f(rv[k][e]) : 0.f;
 #pragma unroll
-    for (int g = 0; g < kNormGroup; ++g)   // rank order
+    for (int g = 0; g < G; ++g)   // rank order
       if (r0 + g < n)
 #pragma unroll
         for (int k = 0; k < NC; ++k)
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(const bf
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
   if constexpr (TPR > 64) {
-    __shared__ float s_ss[kNormThreads / 64];
+    __shared__ float s_ss[BLOCK / 64];
     if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;
     __syncthreads();
     const int w0 = (threadIdx.x / TPR) * (TPR / 64);
@@ -109,39 +112,51 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(const bf
 }
 
 template <int TPR, int NC>
-void launch_norm(const bf16* partials, int n, int64_t M, int H, const bf16* residual, const bf16* w, float eps,
-                 bf16* h_out, bf16* y_out, hipStream_t s) {
-  constexpr int ROWS = kNormThreads / TPR;
+void launch_norm(const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual, const bf16* w,
+                 float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
+  constexpr int BLOCK = TPR > 256 ? TPR : 256, ROWS = BLOCK / TPR;
   const unsigned grid = (unsigned)((M + ROWS - 1) / ROWS);
-  residual_rmsnorm_kernel<TPR, NC><<<grid, kNormThreads, 0, s>>>(partials, n, M, H, residual, w, eps, h_out, y_out);
+  residual_rmsnorm_kernel<TPR, NC>
+      <<<grid, BLOCK, 0, s>>>(partials, n, plane, M, H, residual, w, eps, h_out, y_out);
 }
 
 template <int TPR>
-void launch_norm_tpr(int nc_per, const bf16* partials, int n, int64_t M, int H, const bf16* residual, const bf16* w,
-                     float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
+void launch_norm_tpr(int nc_per, const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
+                     const bf16* w, float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
   switch (nc_per) {
-    case 1: launch_norm<TPR, 1>(partials, n, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 2: launch_norm<TPR, 2>(partials, n, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 3: launch_norm<TPR, 3>(partials, n, M, H, residual, w, eps, h_out, y_out, s); break;
-    default: launch_norm<TPR, 4>(partials, n, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 1: launch_norm<TPR, 1>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 2: launch_norm<TPR, 2>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 3: launch_norm<TPR, 3>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    default: launch_norm<TPR, 4>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
   }
 }
 
 }  // namespace
 
-hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t M, int H, const bf16* residual, const bf16* w,
-                            float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
+int norm_threads_per_row(int64_t M, int H) {
+  const int nc = H / 8;
+  int tpr = 64;
+  while (tpr * 4 < nc) tpr *= 2;   // at most four chunks per thread
+  // few rows: spread each over more waves until the launch has ~8 waves per
+  // CU or a thread per chunk
+  while (tpr < 1024 && tpr < nc && M * (tpr / 64) < 8 * kCUs) tpr *= 2;
+  return tpr;
+}
+
+hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
+                            const bf16* w, float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (H <= 0 || H % 8 || H > 8192 || n < 1) return hipErrorInvalidValue;
-  // rows of up to 64 (128) chunks take one (two) waves; wider rows all four
-  // waves of the workgroup, up to four chunks per thread
   const int nc = H / 8;   // 1..1024
-  if (nc <= 64)
-    launch_norm<64, 1>(partials, n, M, H, residual, w, eps, h_out, y_out, s);
-  else if (nc <= 128)
-    launch_norm<128, 1>(partials, n, M, H, residual, w, eps, h_out, y_out, s);
-  else
-    launch_norm_tpr<256>((nc + 255) / 256, partials, n, M, H, residual, w, eps, h_out, y_out, s);
+  const int tpr = norm_threads_per_row(M, H);
+  const int per = (nc + tpr - 1) / tpr;   // 1..4
+  switch (tpr) {
+    case 64: launch_norm_tpr<64>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 128: launch_norm_tpr<128>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 256: launch_norm_tpr<256>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 512: launch_norm_tpr<512>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    default: launch_norm_tpr<1024>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+  }
   return hipGetLastError();
 }
 

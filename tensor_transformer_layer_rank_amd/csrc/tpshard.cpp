@@ -8,6 +8,8 @@
 // TP": head counts that do not divide are rejected).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../../include/tpshard.h"
 #include "common.h"
 
@@ -375,10 +377,40 @@ int tp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int32_t n_parti
   for (const void* p : ptrs)
     if (!aligned16(p)) return TP_ERR_ALIGN;
   if (M == 0) return TP_OK;
-  return launched(residual_rmsnorm(static_cast<const bf16*>(partials), n_partials, M, cfg->hidden,
+  return launched(residual_rmsnorm(static_cast<const bf16*>(partials), n_partials, M * cfg->hidden, M, cfg->hidden,
                                    static_cast<const bf16*>(residual), static_cast<const bf16*>(norm_w),
                                    cfg->rms_eps, static_cast<bf16*>(h_out), static_cast<bf16*>(y_out),
                                    static_cast<hipStream_t>(stream)));
+}
+
+int tp_sp_rows(const tp_cfg* cfg, int64_t M, int64_t* row0, int64_t* row1) {
+  int st = check_cfg(cfg, nullptr);
+  if (st) return st;
+  if (!row0 || !row1) return TP_ERR_NULL;
+  if (M < 0) return TP_ERR_RANGE;
+  const int64_t per = (M + cfg->tp_size - 1) / cfg->tp_size;
+  *row0 = std::min<int64_t>((int64_t)cfg->tp_rank * per, M);
+  *row1 = std::min<int64_t>((int64_t)(cfg->tp_rank + 1) * per, M);
+  return TP_OK;
+}
+
+int tp_sp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int64_t M, const void* residual_slice,
+                           const void* norm_w, void* h_slice_out, void* y_gathered, void* stream) {
+  int64_t r0 = 0, r1 = 0;
+  int st = tp_sp_rows(cfg, M, &r0, &r1);
+  if (st) return st;
+  if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (cfg->hidden % 8 || cfg->hidden > 8192) return TP_ERR_SHAPE;
+  if (r1 == r0) return TP_OK;   // no token on this rank: nothing to read or write
+  if (!partials || !residual_slice || !norm_w || !h_slice_out || !y_gathered) return TP_ERR_NULL;
+  const void* ptrs[] = {partials, residual_slice, norm_w, h_slice_out, y_gathered};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TP_ERR_ALIGN;
+  const int64_t H = cfg->hidden;
+  return launched(residual_rmsnorm(static_cast<const bf16*>(partials) + r0 * H, cfg->tp_size, M * H, r1 - r0,
+                                   cfg->hidden, static_cast<const bf16*>(residual_slice),
+                                   static_cast<const bf16*>(norm_w), cfg->rms_eps, static_cast<bf16*>(h_slice_out),
+                                   static_cast<bf16*>(y_gathered) + r0 * H, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

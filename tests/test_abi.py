@@ -206,3 +206,24 @@ def test_residual_rmsnorm_validation():
     assert _status(tp.tp_residual_rmsnorm, tp.Cfg(hidden=8200, tp_size=2), A, 2, 5, A, A, A, A, s) == E_SHAPE
     assert _status(tp.tp_residual_rmsnorm, tp.Cfg(hidden=256, tp_size=2, dtype=tp.TP_F32),
                    A, 2, 5, A, A, A, A, s) == E_DTYPE
+
+
+@pytest.mark.parametrize("M,n", [(0, 2), (7, 2), (9, 4), (5, 8), (4096, 2), (1023, 16)])
+def test_sp_rows_match_oracle(M, n):
+    for r in range(n):
+        assert tp.tp_sp_rows(tp.Cfg(hidden=64, tp_size=n, tp_rank=r), M) == O.sp_rows(M, n, r)
+
+
+def test_sp_residual_rmsnorm_validation():
+    s = NullStream()
+    c = tp.Cfg(hidden=256, tp_size=4, tp_rank=3)
+    assert _status(tp.tp_sp_rows, c, -1) == E_RANGE
+    assert _status(tp.tp_sp_rows, tp.Cfg(hidden=256, tp_size=4, tp_rank=4), 8) == E_RANK
+    assert _status(tp.tp_sp_residual_rmsnorm, c, A, 6, A, A, A, A, s) == OK      # rank 3 owns no row of 6
+    assert _status(tp.tp_sp_residual_rmsnorm, c, A, 6, None, A, None, A, s) == OK
+    assert _status(tp.tp_sp_residual_rmsnorm, c, A, -1, A, A, A, A, s) == E_RANGE
+    assert _status(tp.tp_sp_residual_rmsnorm, c, A, 8, A, A, None, A, s) == E_NULL
+    assert _status(tp.tp_sp_residual_rmsnorm, c, A, 8, A, A, A, MIS, s) == E_ALIGN
+    assert _status(tp.tp_sp_residual_rmsnorm, tp.Cfg(hidden=260, tp_size=4), A, 8, A, A, A, A, s) == E_SHAPE
+    assert _status(tp.tp_sp_residual_rmsnorm, tp.Cfg(hidden=256, tp_size=4, dtype=tp.TP_F32),
+                   A, 8, A, A, A, A, s) == E_DTYPE

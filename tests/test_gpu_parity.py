@@ -580,6 +580,7 @@ NORM_CASES = {
     "ragged-h520": (20, 3, 7, 520, None),
     "two-wave-rows-h2056": (24, 5, 11, 2056, None),
     "max-h8192": (21, 1, 5, 8192, None),
+    "h8192-many-rows": (27, 2, 600, 8192, None),
     "h8": (22, 2, 9, 8, None),
 }
 
@@ -634,3 +635,71 @@ def test_residual_rmsnorm_inplace_and_empty():
     tp.tp_residual_rmsnorm(c, y, 2, 0, y, y[0], y, y)
     torch.cuda.synchronize()
     assert (y == 7.0).all()
+
+
+SP_CASES = {
+    # name: (workload id, tp, tokens M, hidden H, rows the oracle checks or None for all)
+    "0.6b-tp2-prefill": (2, 2, 2048, 1024, None),
+    "32b-tp16-prefill": (5, 16, 1024, 5120, [0, 1, 63, 64, 65, 511, 512, 1022, 1023]),
+    "ragged-empty-rank": (25, 4, 9, 520, None),
+    "ragged-short-last": (26, 3, 7, 2056, None),
+}
+
+
+@pytest.mark.parametrize("case", list(SP_CASES))
+def test_sp_residual_rmsnorm(case):
+    """Sequence parallelism: every rank in turn sums its token slice of the
+    ranks' partials into its slice of the residual stream, normalises it and
+    writes its rows of the gathered output.  Each rank's rows against the
+    oracle; the gathered residual bit-equal to the non-sequence-parallel
+    fused step's and the gathered normed rows within one bf16 step of it; a
+    rank's call leaves the other rows of the gathered buffer untouched; a
+    rank with no token writes nothing."""
+    wid, n, M, H, rows = SP_CASES[case]
+    P, R, Wn = synth.norm_inputs(wid, n, M, H)
+    Pg, Rg, Wg = P.to(DEV), R.to(DEV), Wn.to(DEV)
+    Wc = synth.to_f64(Wn)
+    if rows is None:
+        Pc, Rc = synth.to_f64(P), synth.to_f64(R)
+    else:   # sampled rows: the oracle's fused step on those rows alone
+        Pc, Rc = synth.to_f64(P[:, rows]), synth.to_f64(R[rows])
+        h_smp, y_smp = O.residual_rmsnorm(Pc, Rc, Wc, 1e-6)
+    nan = float("nan")
+    y_all = torch.full((M, H), nan, dtype=torch.bfloat16, device=DEV)
+    hs = []
+    for r in range(n):
+        c = tp.Cfg(hidden=H, tp_size=n, tp_rank=r)
+        s, e = tp.tp_sp_rows(c, M)
+        assert (s, e) == O.sp_rows(M, n, r)
+        h = torch.full((e - s, H), nan, dtype=torch.bfloat16, device=DEV)
+        y_one = torch.full((M, H), nan, dtype=torch.bfloat16, device=DEV)
+        tp.tp_sp_residual_rmsnorm(c, Pg, M, Rg[s:e], Wg, h, y_one)
+        tp.tp_sp_residual_rmsnorm(c, Pg, M, Rg[s:e], Wg, h, y_all)
+        torch.cuda.synchronize()
+        outside = torch.ones(M, dtype=torch.bool)
+        outside[s:e] = False
+        assert torch.isnan(y_one.float().cpu()[outside]).all()
+        hs.append(h)
+        if rows is None:
+            if e == s:
+                continue
+            h_ref, y_ref = O.sp_residual_rmsnorm(Pc, Rc[s:e], Wc, c.rms_eps, r)
+            hg, yg = f64(h), f64(y_one[s:e])
+        else:
+            pick = [i for i, m in enumerate(rows) if s <= m < e]
+            if not pick:
+                continue
+            h_ref, y_ref = h_smp[pick], y_smp[pick]
+            hg, yg = f64(h[[rows[i] - s for i in pick]]), f64(y_one[[rows[i] for i in pick]])
+        assert relerr(hg, h_ref) <= TOL_BF16 and relerr(yg, y_ref) <= TOL_BF16
+        assert (np.abs(hg - h_ref) <= bf16_ulp(np.maximum(np.abs(hg), np.abs(h_ref)))).all()
+        assert (np.abs(yg - y_ref) <= 2 * bf16_ulp(np.maximum(np.abs(yg), np.abs(y_ref)))).all()
+    h_full = torch.empty(M, H, dtype=torch.bfloat16, device=DEV)
+    y_full = torch.empty(M, H, dtype=torch.bfloat16, device=DEV)
+    tp.tp_residual_rmsnorm(tp.Cfg(hidden=H, tp_size=n), Pg, n, M, Rg, Wg, h_full, y_full)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(hs).view(torch.int16), h_full.view(torch.int16))
+    # y: the sum of squares is reduced in an order that follows the launch
+    # shape, which depends on the row count; at most one bf16 step apart
+    ya, yf = f64(y_all), f64(y_full)
+    assert (np.abs(ya - yf) <= bf16_ulp(np.maximum(np.abs(ya), np.abs(yf)))).all()
