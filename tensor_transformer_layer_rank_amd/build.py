@@ -39,9 +39,15 @@ FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-
          "-I", os.path.join(ROOT, "include")]
 
 
+# per-source flags: the attention kernel runs one wave per SIMD and keeps its
+# MFMA accumulators in ordinary VGPRs (with AGPR accumulators the compiler
+# copied the output tile between the register files on every key tile)
+EXTRA = {"attn_flash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, asm: bool) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "is not a recognized feature" not in l)
     if r.returncode != 0:
@@ -50,7 +56,7 @@ def _compile(src: str, asm: bool) -> str:
         print(err, file=sys.stderr)
     if asm:
         s = os.path.join(BUILD, src + ".s")
-        subprocess.run([hipcc(), *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", s],
+        subprocess.run([hipcc(), *FLAGS, *EXTRA.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", s],
                        capture_output=True, text=True, check=True)
     return obj
 

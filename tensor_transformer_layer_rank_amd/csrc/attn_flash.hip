@@ -23,6 +23,11 @@
 //    ds_read_b64_tr_b16.
 // The four partial (max, sum, O) are merged through LDS at the end, so a
 // block needs no second pass; prefill blocks run heaviest (latest) first.
+// Prefill, where the block's matrix and vector work is the larger cost,
+// pipelines the tiles: a stage holds K of tile j and V of tile j - 1, so the
+// MFMAs of S for tile i + 1 are in flight while the VALU runs the softmax
+// of tile i.  Decode, bound by the stream of K and V, keeps K and V of one
+// tile per stage (one more tile of loads in flight).
 #include "common.h"
 
 namespace tps {
@@ -69,9 +74,19 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
                : "memory");
 }
 
+// max / sum of a value and its partner 32 lanes away (one lane-swap move)
+__device__ __forceinline__ float pair_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // NWV waves per workgroup, NST ring stages per wave (NST - 1 tiles in
 // flight while one is computed).
-template <int NWV, int NST>
+template <int NWV, int NST, bool PIPE>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_flash_kernel(AttnArgs a, int n_rb) {
   constexpr int NT = NWV * 64;
@@ -133,14 +148,18 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   const i32x4 rk = buffer_rsrc(a.k_cache + slab, valid_bytes);
   const i32x4 rv = buffer_rsrc(a.v_cache + slab, valid_bytes);
   unsigned char* ring = smem + wave * kWaveRingB;
+  // a stage: K of tile kt and V of tile kt (PIPE: of tile kt - 1).  A tile
+  // outside the wave's range may be loaded and is never read; below key 0
+  // the offset wraps past the descriptor bound and reads zero.
   auto dma_tile = [&](int kt, int st) {
     const uint32_t base = lds_addr(ring + st * kStageB);
+    const int vt = PIPE ? kt - 1 : kt;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int key = 4 * i + (lane >> 4);
-      const uint32_t off = (uint32_t)(kt * kKeys + key) * 256u + (uint32_t)(((lane & 15) ^ (key & 15)) << 4);
-      dma16(rk, off, base + i * 1024);
-      dma16(rv, off, base + kTileB + i * 1024);
+      const uint32_t sw = (uint32_t)(((lane & 15) ^ (key & 15)) << 4);
+      dma16(rk, (uint32_t)(kt * kKeys + key) * 256u + sw, base + i * 1024);
+      dma16(rv, (uint32_t)(vt * kKeys + key) * 256u + sw, base + kTileB + i * 1024);
     }
   };
 
@@ -156,9 +175,9 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   const int trg = lane >> 4, tri = lane & 15;
   const int tr_key = 4 * (trg >> 1) + (tri >> 2);          // + sub*16 + rd*8
   const int tr_d = (trg & 1) * 16 + 4 * (tri & 3);         // + db*32
-  auto compute = [&](int kt, int st) {
+  // S^T of the K tile in stage st
+  auto s_tile = [&](int st) -> f32x16 {
     const unsigned char* K = ring + st * kStageB;
-    const unsigned char* V = K + kTileB;
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -167,6 +186,12 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + toff(lr, ks * 2 + lh));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
+    return s;
+  };
+  // online softmax of tile kt's scores s, then O^T += V^T P^T with the V
+  // tile in stage st
+  auto soft_pv = [&](f32x16 s, int kt, int st) {
+    const unsigned char* V = ring + st * kStageB + kTileB;
     const int key0 = kt * kKeys;
     // raw max over this tile's visible scores (the scale is positive)
     float mx = -INFINITY;
@@ -180,7 +205,7 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kQScale;
+    mx = pair_max(mx) * kQScale;
     // Lazy rescale: the exponent base m_run only moves when some row's max
     // passes it by more than kSlack, so P stays below 2^kSlack and O and l,
     // which share the base, stay exact; most tiles skip the O update.
@@ -219,20 +244,49 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
       }
   };
 
-  // this wave's ring: tile w0 + i lives in stage i % NST; tiles up to
-  // i + NST - 1 are in flight while tile i is computed.  The stage a load
-  // refills was read by the previous tile: lgkmcnt(0) first.
   const int n = w1 - w0;
-  for (int j = 0; j < NST - 1 && j < n; ++j) dma_tile(w0 + j, j);
-  for (int i = 0; i < n; ++i) {
-    if (i + NST - 1 < n) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      dma_tile(w0 + i + NST - 1, (i + NST - 1) % NST);
-      wait_vm<(NST - 1) * 2 * kLoads>();
-    } else {
-      wait_vm<0>();
+  if constexpr (!PIPE) {
+    // tile w0 + i lives in stage i % NST; tiles up to i + NST - 1 are in
+    // flight while tile i is computed.  The stage a load refills was read
+    // by the previous tile: lgkmcnt(0) first.
+    for (int j = 0; j < NST - 1 && j < n; ++j) dma_tile(w0 + j, j);
+    for (int i = 0; i < n; ++i) {
+      if (i + NST - 1 < n) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        dma_tile(w0 + i + NST - 1, (i + NST - 1) % NST);
+        wait_vm<(NST - 1) * 2 * kLoads>();
+      } else {
+        wait_vm<0>();
+      }
+      soft_pv(s_tile(i % NST), w0 + i, i % NST);
     }
-    compute(w0 + i, i % NST);
+  } else if (n > 0) {
+    // stage j = {K of tile w0 + j, V of tile w0 + j - 1}, j = 0 .. n, in
+    // buffer j % 2.  Iteration i reads stage i + 1 (K for S of tile i + 1,
+    // V for tile i), then refills its buffer with stage i + 3.
+    static_assert(NST == 2, "the pipelined loop uses two stages");
+    constexpr int SL = 2 * kLoads;         // loads per stage
+    dma_tile(w0, 0);
+    dma_tile(w0 + 1, 1);
+    wait_vm<SL>();
+    f32x16 s_cur = s_tile(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage 0 read
+    if (2 <= n) dma_tile(w0 + 2, 0);
+    for (int i = 0; i < n; ++i) {
+      const int st = (i + 1) & 1;
+      if (i + 2 <= n)
+        wait_vm<SL>();
+      else
+        wait_vm<0>();
+      f32x16 s_next = s_cur;
+      if (i + 1 < n) s_next = s_tile(st);
+      soft_pv(s_cur, w0 + i, st);
+      s_cur = s_next;
+      if (i + 3 <= n) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage i + 1 read
+        dma_tile(w0 + i + 3, st);
+      }
+    }
   }
 
   // merge the four waves' partials through LDS (the area overlaps the rings)
@@ -245,7 +299,7 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) row[db * 32 + 8 * (e >> 2) + 4 * lh + (e & 3)] = o[db][e];
-    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float l = pair_sum(l_run);
     if (lh == 0) {
       mml[(wave * 32 + lr) * 2] = m_run;
       mml[(wave * 32 + lr) * 2 + 1] = l;
@@ -293,7 +347,10 @@ hipError_t attn_flash(const AttnArgs& a, hipStream_t s) {
   if (a.lkv <= 0 || a.lq % a.lkv != 0 || rep > 32) return hipErrorInvalidValue;
   const int n_rb = (a.T + 31) / 32;
   const int64_t blocks = a.T == 1 ? (int64_t)a.B * a.lkv : (int64_t)a.B * a.lq * n_rb;
-  attn_flash_kernel<4, 2><<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
+  if (a.T == 1)
+    attn_flash_kernel<4, 2, false><<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
+  else
+    attn_flash_kernel<4, 2, true><<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
   return hipGetLastError();
 }
 

@@ -28,9 +28,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
 }
 
-// 16-byte chunk position inside a 128-byte tile row: 16 consecutive rows
-// land on 16 distinct 16-byte slots of the 256-byte bank space.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// 16-byte chunk position inside a tile row of BK bf16 (128 or 64 bytes):
+// 16 consecutive rows land on 16 distinct 16-byte slots of the 256-byte
+// bank space.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  static_assert(BK == 64 || BK == 32, "tile rows of 128 or 64 bytes");
+  return BK == 64 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -114,7 +119,9 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
   *reinterpret_cast<bf16x8*>(dst + 8 * j) = o;
 }
 // the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
-constexpr bool qkv_tile_ok(int bm, int bn, int stages) { return bn % 128 == 0 && bm * bn * 4 <= stages * (bm + bn) * 128; }
+constexpr bool qkv_tile_ok(int bm, int bn, int stages, int bk = 64) {
+  return bn % 128 == 0 && bm * bn * 4 <= stages * (bm + bn) * bk * 2;
+}
 
 // Default LDS stages per tile shape: as many as let two workgroups share a
 // CU's 160 KB (at least 2, at most 6).  Weight-streaming shapes (few rows)
@@ -123,15 +130,15 @@ constexpr int gemm_stages(int bm, int bn) {
   return (81920 / ((bm + bn) * 64 * 2)) > 6 ? 6 : ((81920 / ((bm + bn) * 64 * 2)) < 2 ? 2 : 81920 / ((bm + bn) * 64 * 2));
 }
 // waves per SIMD that one CU holds for a tile shape and ring depth (LDS-limited)
-constexpr int gemm_waves_per_simd(int bm, int bn, int nw, int stages) {
-  return (nw / 4 < 1 ? 1 : nw / 4) * (163840 / (stages * (bm + bn) * 64 * 2));
+constexpr int gemm_waves_per_simd(int bm, int bn, int nw, int stages, int bk = 64) {
+  return (nw / 4 < 1 ? 1 : nw / 4) * (163840 / (stages * (bm + bn) * bk * 2));
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M, int S>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M, int S, int BK = 64>
 __global__ __launch_bounds__(WGM * WGN * 64)
-__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd(BM, BN, WGM * WGN, S), gemm_waves_per_simd(BM, BN, WGM * WGN, S))))
+__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd(BM, BN, WGM * WGN, S, BK),
+                                   gemm_waves_per_simd(BM, BN, WGM * WGN, S, BK))))
 void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
-  constexpr int BK = 64;
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -167,21 +174,23 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   }
   const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
 
-  // Tile loads.  Wave w fills 8-row groups g = w, w + NW, ... of each
-  // stage; lane l of a group writes LDS row 8g + l/8, physical chunk l%8,
-  // and so fetches the logical chunk that the swizzle puts there.  One
+  // Tile loads.  One load instruction fills RPI rows (1 KB): wave w fills
+  // row groups g = w, w + NW, ... of each stage; lane l of a group writes
+  // LDS row RPI*g + l/KC, physical chunk l%KC, and so fetches the logical
+  // chunk that the swizzle puts there.  One
   // buffer descriptor per operand covers the tile's rows from column 0 to
   // the end of the matrix; a block at column k0 adds 2*k0 to the lane
   // offsets, so the range check drops exactly what lies past the matrix
   // (rows past M or N, and columns past the last row's end).  Those zeros
   // only feed outputs that are never stored, or are cleared by zero_tail.
   constexpr int NW = WGM * WGN;
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "8-row groups must split evenly");
-  static_assert(EPI != EPI_SILU_BF16 || (BN / 2) % 8 == 0, "gate/up halves must hold whole groups");
-  constexpr int A_G = BM / (8 * NW), B_G = BN / (8 * NW);
+  constexpr int RPI = 512 / BK;             // rows per 1 KB load instruction
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "row groups must split evenly");
+  static_assert(EPI != EPI_SILU_BF16 || (BN / 2) % RPI == 0, "gate/up halves must hold whole groups");
+  constexpr int A_G = BM / (RPI * NW), B_G = BN / (RPI * NW);
   constexpr int NV = A_G + B_G;             // direct-to-LDS loads per block per wave
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int grow = lane >> 3, gpc = lane & 7;
+  const int grow = lane / KC, gpc = lane % KC;
   const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
   // B rows of this tile: [b_row0, +BN) or, for silu, [gate0, +BN/2) and [up0, +BN/2)
   const int64_t nrow0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) : (int64_t)tn * BN;
@@ -195,19 +204,19 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   for (int v = 0; v < NV; ++v) {
     const bool isA = v < A_G;
     const int g = wave + (isA ? v : v - A_G) * NW;
-    const bool up = !isA && EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-    const int row = g * 8 + grow - (up ? BN / 2 : 0);
-    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + ((gpc ^ ((row >> 1) & 7)) << 4));
+    const bool up = !isA && EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
+    const int row = g * RPI + grow - (up ? BN / 2 : 0);
+    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + (swz<BK>(row, gpc) << 4));
   }
   auto dma_slice = [&](int v, int64_t k0, int buf) {
     bf16* st = smem + buf * STAGE;
     const uint32_t ko = (uint32_t)(k0 * 2);
     if (v < A_G) {
-      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * 8 * BK);
+      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
     } else {
       const int g = wave_u + (v - A_G) * NW;
-      const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * 8 * BK);
+      const bool up = EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
+      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
     }
   };
   // The last block may end inside the 64-wide K window: its columns at or
@@ -217,7 +226,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     bf16* st = smem + buf * STAGE;
     for (int q = tid; q < (BM + BN) * KC; q += NT) {
       const int row = q / KC, lc = q % KC;
-      if (k0 + lc * 8 >= kend) *reinterpret_cast<u32x4*>(st + row * BK + swz(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
+      if (k0 + lc * 8 >= kend) *reinterpret_cast<u32x4*>(st + row * BK + swz<BK>(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
     }
   };
   // tile-local column of the j-th 32-wide n-block of this wave
@@ -259,10 +268,10 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     if (x == 0 || x > TN) {
       const int i = x == 0 ? 0 : x - TN;
       const int row = wm * WM + i * 32 + lr;
-      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
+      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
     } else {
       const int row = ncol(x - 1) + lr;
-      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
+      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
     }
   };
   auto mfma_pair = [&](int fs, int pr) {
@@ -426,7 +435,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     return;
   }
   if constexpr (EPI == EPI_QKV) {
-    static_assert(qkv_tile_ok(BM, BN, S), "QKV tile must cover whole heads and fit the ring");
+    static_assert(qkv_tile_ok(BM, BN, S, BK), "QKV tile must cover whole heads and fit the ring");
     // stage the fp32 tile [BM][BN] in LDS (16-byte chunk c of row r at
     // c ^ ((r >> 2) & 1): the two half-waves write rows 4 apart), then
     // finish it 16 lanes per (row, head)
@@ -543,12 +552,11 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 // dispatcher deals workgroups round-robin) and takes every G-th tile of its
 // XCD's range, G = the XCD's workgroup count, so the CUs of one XCD work on
 // neighbouring tiles at any time and share A and B panels in its L2.
-template <int BM, int BN, int WGM, int WGN, int EPI, int GROUP_M, int S>
+template <int BM, int BN, int WGM, int WGN, int EPI, int GROUP_M, int S, int BK = 64>
 __global__ __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   static_assert(EPI == EPI_BF16 || EPI == EPI_SILU_BF16, "bf16 outputs only");
-  constexpr int BK = 64;
   constexpr int NW = WGM * WGN, NT = NW * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -591,17 +599,19 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     nrow0 = (int64_t)(r / gm) * (EPI == EPI_SILU_BF16 ? BN / 2 : BN);
   };
 
-  constexpr int A_G = BM / (8 * NW), B_G = BN / (8 * NW), NV = A_G + B_G;
-  const int grow = lane >> 3, gpc = lane & 7;
+  constexpr int RPI = 512 / BK;             // rows per 1 KB load instruction
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "row groups must split evenly");
+  constexpr int A_G = BM / (RPI * NW), B_G = BN / (RPI * NW), NV = A_G + B_G;
+  const int grow = lane / KC, gpc = lane % KC;
   const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
   uint32_t voff[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const bool isA = v < A_G;
     const int g = wave + (isA ? v : v - A_G) * NW;
-    const bool up = !isA && EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-    const int row = g * 8 + grow - (up ? BN / 2 : 0);
-    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + ((gpc ^ ((row >> 1) & 7)) << 4));
+    const bool up = !isA && EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
+    const int row = g * RPI + grow - (up ? BN / 2 : 0);
+    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + (swz<BK>(row, gpc) << 4));
   }
   // descriptors of the tile that the loads are filling (they run ahead of
   // the MFMAs by S - 1 blocks, so into the next tile near a tile's end)
@@ -622,11 +632,11 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       if (v < A_G) {
-        dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * 8 * BK);
+        dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
       } else {
         const int g = wave_u + (v - A_G) * NW;
-        const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-        dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * 8 * BK);
+        const bool up = EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
+        dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
       }
     }
     if (++dkb == nk) {
@@ -639,11 +649,11 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     bf16* st = smem + buf * STAGE;
     const uint32_t ko = (uint32_t)dkb * (BK * 2);
     if (v < A_G) {
-      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * 8 * BK);
+      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
     } else {
       const int g = wave_u + (v - A_G) * NW;
-      const bool up = EPI == EPI_SILU_BF16 && g * 8 >= BN / 2;
-      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * 8 * BK);
+      const bool up = EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
+      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
     }
   };
   auto zero_tail = [&](int buf) __attribute__((always_inline)) {
@@ -651,7 +661,7 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int64_t k0 = (int64_t)(nk - 1) * BK;
     for (int q = tid; q < (BM + BN) * KC; q += NT) {
       const int row = q / KC, lc = q % KC;
-      if (k0 + lc * 8 >= K) *reinterpret_cast<u32x4*>(st + row * BK + swz(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
+      if (k0 + lc * 8 >= K) *reinterpret_cast<u32x4*>(st + row * BK + swz<BK>(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto ncol = [&](int j) __attribute__((always_inline)) -> int {
@@ -682,10 +692,10 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     if (x == 0 || x > TN) {
       const int i = x == 0 ? 0 : x - TN;
       const int row = wm * WM + i * 32 + lr;
-      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz(row, c) * 8);
+      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
     } else {
       const int row = ncol(x - 1) + lr;
-      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz(row, c) * 8);
+      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
     }
   };
   auto mfma_pair = [&](int fs, int pr) __attribute__((always_inline)) {
