@@ -398,17 +398,22 @@ def test_qkv_attn_wide_prefill_sampled():
 
 
 @pytest.mark.parametrize("name", list(MID))
-@pytest.mark.parametrize("phase", ["prefill", "prefill-after-past", "decode", "decode-ctx1", "decode-long"])
+@pytest.mark.parametrize("phase", ["prefill", "prefill-after-past", "prefill-tiny", "prefill-few-tiles", "decode",
+                                   "decode-ctx1", "decode-long"])
 def test_qkv_attn_mid(name, phase):
     """prefill: 2 sequences of 300 tokens; prefill-after-past: 77 new tokens
-    after 150 cached ones; decode: 8 sequences; decode-ctx1: 3 sequences, one
-    key; decode-long: 2 sequences at context 3000 (the key range split among
-    a block's waves and merged).  These grids are small, so the one-pass
-    flash kernel runs every phase."""
+    after 150 cached ones; prefill-tiny: 3 sequences of 2 tokens (one key
+    tile: three of a block's four waves have none); prefill-few-tiles: 40
+    tokens after 60 cached ones (0 to 2 tiles per wave, the pipelined loop's
+    short cases); decode: 8 sequences; decode-ctx1: 3 sequences, one key;
+    decode-long: 2 sequences at context 3000 (the key range split among a
+    block's waves and merged).  These grids are small, so the one-pass flash
+    kernel runs every phase."""
     w, wid = MID[name], MID_WID[name]
     W = synth.full_weights(wid, w)
     Wg = {k: v.to(DEV) for k, v in W.items()}
     B, T, past, S_max = {"prefill": (2, 300, 0, 320), "prefill-after-past": (2, 77, 150, 240),
+                         "prefill-tiny": (3, 2, 0, 4), "prefill-few-tiles": (2, 40, 60, 128),
                          "decode": (8, 1, 299, 310), "decode-ctx1": (3, 1, 0, 4),
                          "decode-long": (2, 1, 2999, 3000)}[phase]
     for r in range(w["tp"]):
