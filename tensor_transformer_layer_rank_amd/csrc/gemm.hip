@@ -938,8 +938,8 @@ struct Variant {
 };
 enum VariantId { V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V_COUNT };
 constexpr Variant kVariants[V_COUNT] = {
-    {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.65f, true},
-    {128, 128, 2, 2, 1.20f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
+    {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.59f, true},
+    {128, 128, 2, 2, 1.08f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
     {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},
 };
 // Constants fitted to a sweep of every (variant, split) plan over the
@@ -1111,8 +1111,8 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
   switch (pl.v) {
     case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, epi, pl, scratch, s);
     case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, epi, pl, scratch, s);
-    case V128x128_4: return launch_tile<128, 128, 2, 2, 4>(p, epi, pl, scratch, s);
-    case V128x128_2: return launch_tile<128, 128, 2, 2, 2>(p, epi, pl, scratch, s);
+    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, epi, pl, scratch, s);
+    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, epi, pl, scratch, s);
     case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, epi, pl, scratch, s);
     case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s);
     case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s);
