@@ -866,28 +866,44 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 }
 
 // Sums split-K partials [splits, M, N] in a fixed order and applies the
-// final epilogue.
+// final epilogue.  Four consecutive columns per thread; the loads of all
+// splits (at most kMaxSplits) are issued before the first add, so a thread
+// waits for memory once, not once per split.
+constexpr int kMaxSplits = 8;
+
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ part, int splits, int64_t M,
                                                      int64_t N, void* out, int64_t ldc, int64_t li) {
   const int64_t cols = EPI == EPI_SILU_BF16 ? li : N;
-  const int64_t total = M * cols;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t m = i / cols, n = i - m * cols;
-    if (EPI == EPI_SILU_BF16) {
-      float g = 0.f, u = 0.f;
-      for (int z = 0; z < splits; ++z) {
-        g += part[((int64_t)z * M + m) * N + n];
-        u += part[((int64_t)z * M + m) * N + li + n];
+  const int64_t quads = M * (cols / 4);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / (cols / 4), n = (i - m * (cols / 4)) * 4;
+    f32x4 g[kMaxSplits], u[kMaxSplits];
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z)
+      if (z < splits) {
+        const float* src = part + ((int64_t)z * M + m) * N + n;
+        g[z] = *reinterpret_cast<const f32x4*>(src);
+        if (EPI == EPI_SILU_BF16) u[z] = *reinterpret_cast<const f32x4*>(src + li);
       }
-      static_cast<bf16*>(out)[m * ldc + n] = f2bf(g / (1.f + __expf(-g)) * u);
-    } else {
-      float s = 0.f;
-      for (int z = 0; z < splits; ++z) s += part[((int64_t)z * M + m) * N + n];
-      if (EPI == EPI_BF16)
-        static_cast<bf16*>(out)[m * ldc + n] = f2bf(s);
+    f32x4 sg = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z)
+      if (z < splits) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sg[e] += g[z][e];
+          if (EPI == EPI_SILU_BF16) su[e] += u[z][e];
+        }
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (EPI == EPI_SILU_BF16)
+        static_cast<bf16*>(out)[m * ldc + n + e] = f2bf(sg[e] / (1.f + __expf(-sg[e])) * su[e]);
+      else if (EPI == EPI_BF16)
+        static_cast<bf16*>(out)[m * ldc + n + e] = f2bf(sg[e]);
       else
-        static_cast<float*>(out)[m * ldc + n] = s;
+        static_cast<float*>(out)[m * ldc + n + e] = sg[e];
     }
   }
 }
@@ -903,17 +919,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv(const float* __restrict
   for (int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; u < M * heads; u += (int64_t)gridDim.x * 16) {
     const int64_t m = u / heads;
     const int h = (int)(u - m * heads);
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < splits; ++z) {
-      const float* src = part + ((int64_t)z * M + m) * N + (int64_t)h * 128 + 8 * j;
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+    f32x4 v0[kMaxSplits], v1[kMaxSplits];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] += v0[e];
-        x[4 + e] += v1[e];
+    for (int z = 0; z < kMaxSplits; ++z)
+      if (z < splits) {
+        const float* src = part + ((int64_t)z * M + m) * N + (int64_t)h * 128 + 8 * j;
+        v0[z] = *reinterpret_cast<const f32x4*>(src);
+        v1[z] = *reinterpret_cast<const f32x4*>(src + 4);
       }
-    }
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < kMaxSplits; ++z)
+      if (z < splits) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] += v0[z][e];
+          x[4 + e] += v1[z][e];
+        }
+      }
     qkv_finish(a, x, m, h, j, cr);
   }
 }
@@ -986,10 +1009,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split) {
   Plan best{V256x256, 1, K, 0, 0};
   double best_cost = 1e300;
   const int64_t kblocks = (K + 63) / 64;
+  // the reductions read the partials four columns at a time
+  const bool quad_cols = N % 4 == 0 && (epi != EPI_SILU_BF16 || (N / 2) % 4 == 0);
   for (int vi = 0; vi < V_COUNT; ++vi) {
     const Variant& v = kVariants[vi];
-    for (int64_t sp = 1; sp <= 8; ++sp) {
-      if (sp > 1 && (!allow_split || kblocks < 4 * sp)) break;
+    for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
+      if (sp > 1 && (!allow_split || !quad_cols || kblocks < 4 * sp)) break;
       if (epi == EPI_SILU_BF16 && !v.silu) continue;
       if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
@@ -1016,7 +1041,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     dim3 grid(pl.tiles_m * pl.tiles_n, pl.splits);
     gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
-    int64_t g = (p.M * cols + 255) / 256;
+    int64_t g = (p.M * (cols / 4) + 255) / 256;
     if (g > 4096) g = 4096;
     if (epi == EPI_QKV) {
       int64_t gq = (p.M * (p.N / 128) * 16 + 255) / 256;
