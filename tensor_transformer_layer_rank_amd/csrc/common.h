@@ -20,6 +20,29 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+
+// Cross-lane sums without LDS round trips: DPP lane permutations inside each
+// 16-lane row (xor 1 and xor 2 as quad permutes, then the 8- and 16-lane
+// mirrors, each pairing a lane with one of the other half), then the gfx950
+// row-pair and half-wave swaps.  Every lane receives the sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+  v = row_sum16(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // RNE (v_cvt_pk_bf16_f32)
 
 // --- GEMM -----------------------------------------------------------------

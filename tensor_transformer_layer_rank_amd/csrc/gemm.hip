@@ -66,46 +66,61 @@ __device__ __forceinline__ void wait_vm() {
 // (v[i], v[i+64]) turns by pos * theta^(-2i/128) (Qwen3 conventions, which
 // the pages import without printing).
 //
-// 16 lanes hold one (row, head): lane j has d = 8j .. 8j+7, so the pair
-// partner of lane j is lane j ^ 8 and the norm is a 16-lane reduction.
-// rope_coef() gives theta^(-2i/128) / (2 pi) for the lane's 8 indices i; the
-// angle in revolutions is reduced in double (positions reach ~1e6) before the
-// fp32 sine and cosine.
-__device__ __forceinline__ void rope_coef(float theta, int j, double (&cr)[8]) {
+// 16 lanes hold one (row, head): lane j has d = 4j .. 4j+3 and their RoPE
+// partners d + 64, so the rotation stays inside the lane and the norm is a
+// 16-lane reduction.  rope_coef() gives theta^(-2i/128) / (2 pi) for the
+// lane's four indices i = 4j + e as a float head plus tail; rope_sincos()
+// forms the angle in revolutions, pos * coef, without losing the fraction
+// (the head product's rounding error by FMA, the integer part dropped before
+// the small terms are added; positions are exact in fp32 below 2^24), and
+// the hardware sine and cosine take revolutions.
+struct RopeCoef {
+  float hi[4], lo[4];
+};
+__device__ __forceinline__ RopeCoef rope_coef(float theta, int j) {
+  RopeCoef c;
   const double l2t = log2((double)theta);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int i = (8 * j + e) & 63;
-    cr[e] = exp2(-(double)(2 * i) / 128.0 * l2t) * 0.159154943091895335768883;
+  for (int e = 0; e < 4; ++e) {
+    const double cr = exp2(-(double)(2 * (4 * j + e)) / 128.0 * l2t) * 0.159154943091895335768883;
+    c.hi[e] = (float)cr;
+    c.lo[e] = (float)(cr - (double)c.hi[e]);
   }
+  return c;
 }
+__device__ __forceinline__ void rope_sincos(int pos, float hi, float lo, float& sn, float& cs) {
+  const float p = (float)pos;
+  const float q = p * hi;
+  const float err = __builtin_fmaf(p, hi, -q);   // q + err == p * hi exactly
+  const float rev = (q - __builtin_rintf(q)) + __builtin_fmaf(p, lo, err);
+  sn = __builtin_amdgcn_sinf(rev);
+  cs = __builtin_amdgcn_cosf(rev);
+}
+// x[0..3] hold d = 4j .. 4j+3 of (row m, head h), x[4..7] hold d + 64
 __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
-                                           const double (&cr)[8]) {
+                                           const RopeCoef& rc) {
   const int b = (int)(m / a.T), t = (int)(m - (int64_t)b * a.T);
   const int pos = a.past + t;
   if (h < a.lq + a.lkv) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    ss += __shfl_xor(ss, 8, 64);
+    ss = row_sum16(ss);
     const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>((h < a.lq ? a.q_norm_w : a.k_norm_w) + 8 * j);
-    const bf16x8 w = __builtin_bit_cast(bf16x8, wv);
+    const bf16* wp = (h < a.lq ? a.q_norm_w : a.k_norm_w) + 4 * j;
+    const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(wp), w1 = *reinterpret_cast<const bf16x4*>(wp + 64);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= inv * bf2f(w[e]);
-    float xp[8];
+    for (int e = 0; e < 4; ++e) {
+      x[e] *= inv * bf2f(w0[e]);
+      x[4 + e] *= inv * bf2f(w1[e]);
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xp[e] = __shfl_xor(x[e], 8, 64);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      double rev = (double)pos * cr[e];
-      rev -= rint(rev);
-      const float ang = (float)(rev * 6.283185307179586476925);
-      const float sn = __sinf(ang), cs = __cosf(ang);
-      x[e] = j < 8 ? x[e] * cs - xp[e] * sn : x[e] * cs + xp[e] * sn;
+    for (int e = 0; e < 4; ++e) {
+      float sn, cs;
+      rope_sincos(pos, rc.hi[e], rc.lo[e], sn, cs);
+      const float x1 = x[e], x2 = x[4 + e];
+      x[e] = x1 * cs - x2 * sn;
+      x[4 + e] = x2 * cs + x1 * sn;
     }
   }
   bf16* dst;
@@ -115,8 +130,10 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
     dst = a.k_cache + (((int64_t)b * a.lkv + (h - a.lq)) * a.S_max + pos) * 128;
   else
     dst = a.v_cache + (((int64_t)b * a.lkv + (h - a.lq - a.lkv)) * a.S_max + pos) * 128;
-  const bf16x8 o = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3]), f2bf(x[4]), f2bf(x[5]), f2bf(x[6]), f2bf(x[7])};
-  *reinterpret_cast<bf16x8*>(dst + 8 * j) = o;
+  const bf16x4 o0 = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
+  const bf16x4 o1 = {f2bf(x[4]), f2bf(x[5]), f2bf(x[6]), f2bf(x[7])};
+  *reinterpret_cast<bf16x4*>(dst + 4 * j) = o0;
+  *reinterpret_cast<bf16x4*>(dst + 64 + 4 * j) = o1;
 }
 // the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
 constexpr bool qkv_tile_ok(int bm, int bn, int stages, int bk = 64) {
@@ -451,8 +468,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
           st[st_off(wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), ncol(j) + lr)] = acc[i][j][e];
     __syncthreads();
     const int j16 = tid & 15;
-    double cr[8];
-    rope_coef(p.qkv.theta, j16, cr);
+    const RopeCoef rc = rope_coef(p.qkv.theta, j16);
     constexpr int HPT = BN / 128;                      // heads per tile
     const int heads = (int)(p.N / 128);
     for (int u = tid >> 4; u < BM * HPT; u += NT / 16) {
@@ -460,10 +476,11 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       const int64_t m = m0 + r;
       const int h = tn * HPT + hh;
       if (m >= M || h >= heads) continue;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = st[st_off(r, hh * 128 + 8 * j16 + e)];
-      qkv_finish(p.qkv, x, m, h, j16, cr);
+      // four consecutive columns are one 16-byte group of the staged tile
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + st_off(r, hh * 128 + 4 * j16));
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + st_off(r, hh * 128 + 64 + 4 * j16));
+      float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      qkv_finish(p.qkv, x, m, h, j16, rc);
     }
     return;
   }
@@ -914,8 +931,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv(const float* __restrict
                                                          int64_t N, QkvArgs a) {
   const int heads = (int)(N / 128);
   const int j = threadIdx.x & 15;
-  double cr[8];
-  rope_coef(a.theta, j, cr);
+  const RopeCoef rc = rope_coef(a.theta, j);
   for (int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; u < M * heads; u += (int64_t)gridDim.x * 16) {
     const int64_t m = u / heads;
     const int h = (int)(u - m * heads);
@@ -923,9 +939,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv(const float* __restrict
 #pragma unroll
     for (int z = 0; z < kMaxSplits; ++z)
       if (z < splits) {
-        const float* src = part + ((int64_t)z * M + m) * N + (int64_t)h * 128 + 8 * j;
+        const float* src = part + ((int64_t)z * M + m) * N + (int64_t)h * 128 + 4 * j;
         v0[z] = *reinterpret_cast<const f32x4*>(src);
-        v1[z] = *reinterpret_cast<const f32x4*>(src + 4);
+        v1[z] = *reinterpret_cast<const f32x4*>(src + 64);
       }
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -937,7 +953,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv(const float* __restrict
           x[4 + e] += v1[z][e];
         }
       }
-    qkv_finish(a, x, m, h, j, cr);
+    qkv_finish(a, x, m, h, j, rc);
   }
 }
 

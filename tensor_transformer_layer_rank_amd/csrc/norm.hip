@@ -88,8 +88,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel
       __builtin_nontemporal_store(hb, reinterpret_cast<bf16x8*>(h_out + row + (int64_t)(t + k * TPR) * 8));
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  ss = wave_sum64(ss);
   if constexpr (TPR > 64) {
     __shared__ float s_ss[BLOCK / 64];
     if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;
