@@ -39,10 +39,12 @@ FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-
          "-I", os.path.join(ROOT, "include")]
 
 
-# per-source flags: the attention kernel runs one wave per SIMD and keeps its
-# MFMA accumulators in ordinary VGPRs (with AGPR accumulators the compiler
-# copied the output tile between the register files on every key tile)
-EXTRA = {"attn_flash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source flags: the attention kernels run one wave per SIMD and keep
+# their MFMA accumulators in ordinary VGPRs (with AGPR accumulators the
+# compiler copied the output tiles between the register files on every key
+# tile; measured 10-20% slower)
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"attn_flash.hip": _VGPR_MFMA, "attn_prefill.hip": _VGPR_MFMA}
 
 
 def _compile(src: str, asm: bool) -> str:

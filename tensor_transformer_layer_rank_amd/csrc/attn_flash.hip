@@ -74,16 +74,6 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
                : "memory");
 }
 
-// max / sum of a value and its partner 32 lanes away (one lane-swap move)
-__device__ __forceinline__ float pair_max(float v) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float pair_sum(float v) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
 // NWV waves per workgroup, NST ring stages per wave (NST - 1 tiles in
 // flight while one is computed).
 template <int NWV, int NST, bool PIPE>

@@ -217,7 +217,7 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hw][kb][e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kQScale;
+      mx = pair_max(mx) * kQScale;
       // Lazy rescale: the exponent base m_run only moves when some row's max
       // passes it by more than kSlack, so P stays below 2^kSlack and O and
       // l, which share the base, stay exact; most tiles skip the O update.
@@ -310,7 +310,7 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
   __syncthreads();   // the staging area overlaps the ring
 #pragma unroll
   for (int hw = 0; hw < HW; ++hw) {
-    const float l = l_run[hw] + __shfl_xor(l_run[hw], 32, 64);
+    const float l = pair_sum(l_run[hw]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16* so = stage_region(wave * HW + hw);
 #pragma unroll

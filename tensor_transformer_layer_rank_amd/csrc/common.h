@@ -36,6 +36,15 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<0x140>(v);   // row_mirror
   return v;
 }
+// max / sum of a value and its partner 32 lanes away (one lane-swap move)
+__device__ __forceinline__ float pair_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 __device__ __forceinline__ float wave_sum64(float v) {
   v = row_sum16(v);
   const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
