@@ -36,6 +36,57 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<0x140>(v);   // row_mirror
   return v;
 }
+// Greedy candidates (value, index): better = larger value, or equal value
+// and smaller index; index < 0 is "none".  A total order, so any pairing of
+// lanes reduces to the same winner.
+__device__ __forceinline__ bool cand_better(float v, int i, float bv, int bi) {
+  return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
+}
+template <int CTRL>
+__device__ __forceinline__ void cand_step_dpp(float& v, int& i) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false);
+  if (cand_better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+// best candidate of each 32-lane half of the wave, in all its lanes
+__device__ __forceinline__ void cand_best32(float& v, int& i) {
+  cand_step_dpp<0xB1>(v, i);    // quad_perm [1,0,3,2]
+  cand_step_dpp<0x4E>(v, i);    // quad_perm [2,3,0,1]
+  cand_step_dpp<0x141>(v, i);   // row_half_mirror
+  cand_step_dpp<0x140>(v, i);   // row_mirror
+  const auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto pi = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+  // each lane sees its own row's value in one output and the paired row's in
+  // the other; take the better of the two
+  const float v0 = __uint_as_float(pv[0]), v1 = __uint_as_float(pv[1]);
+  const int i0 = (int)pi[0], i1 = (int)pi[1];
+  if (cand_better(v1, i1, v0, i0)) {
+    v = v1;
+    i = i1;
+  } else {
+    v = v0;
+    i = i0;
+  }
+}
+// best candidate of the whole wave, in all lanes
+__device__ __forceinline__ void cand_best64(float& v, int& i) {
+  cand_best32(v, i);
+  const auto pv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto pi = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+  const float v0 = __uint_as_float(pv[0]), v1 = __uint_as_float(pv[1]);
+  const int i0 = (int)pi[0], i1 = (int)pi[1];
+  if (cand_better(v1, i1, v0, i0)) {
+    v = v1;
+    i = i1;
+  } else {
+    v = v0;
+    i = i0;
+  }
+}
+
 // max / sum of a value and its partner 32 lanes away (one lane-swap move)
 __device__ __forceinline__ float pair_max(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -421,15 +421,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
             bi = (int)col;
           }
         }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) {
-          const float ov = __shfl_xor(bv, off, 64);
-          const int oi = __shfl_xor(bi, off, 64);
-          if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-          }
-        }
+        cand_best32(bv, bi);
         if (lr == 0) {
           const int r = wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
           cv[wn * BM + r] = bv;

@@ -19,21 +19,11 @@ namespace {
 
 // better candidate: larger value, or equal value and smaller index; an
 // index < 0 marks "none"
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
-}
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return cand_better(v, i, bv, bi); }
 
 // best of 256 threads' (value, column) pairs -> thread 0
 __device__ __forceinline__ void block_best(float& bv, int& bi) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off, 64);
-    const int oi = __shfl_xor(bi, off, 64);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
+  cand_best64(bv, bi);
   __shared__ float s_v[4];
   __shared__ int s_i[4];
   const int tid = threadIdx.x;
