@@ -278,7 +278,7 @@ def run_bench(args):
         "phase_us": {p: round(v * 1e6, 2) for p, v in ph.items()},
         "work": {"prefill_GFLOP": round(prefill_flops / 1e9, 2), "lm_head_GFLOP": round(lm_flops / 1e9, 2),
                  "decode_MB": round(dec_bytes / 1e6, 2), "decode_KV_MB": round(db["kv"] / 1e6, 2)},
-        "roofline": {"kernel": "gemm_kernel (tp_lm_head, one launch)", "bound": "mfma",
+        "roofline": {"kernel": "gemm_persist_kernel (tp_lm_head, one launch per step)", "bound": "mfma",
                      "achieved": round(lm_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "algorithmic_bytes_per_launch": 2 * (n_ids * H + nv * H + n_ids * nv),
