@@ -8,13 +8,17 @@
  *   - the row-parallel o_proj / down_proj, which leave partial sums,
  *   - GQA attention over the rank's local heads (kv heads replicated when the
  *     tensor-parallel size exceeds the kv-head count),
- *   - the vocab-parallel masked embedding and the lm_head vocab slice.
+ *   - the vocab-parallel masked embedding and the lm_head vocab slice,
+ *   - the greedy decode head: per-shard (max, first id) candidates fused into
+ *     the logits GEMM, and their combine across shards,
+ *   - the residual add of the summed row-parallel partials with the next
+ *     RMSNorm, and its sequence-parallel form on the rank's token slice.
  *
  * Sources (web pages; the section that defines each operation is cited at
  * each entry point):
  *   [TPS]    "Tensor parallelism from scratch" (ai-infra-handbooks):
  *            "Two ways to split", "Implementation", "KV heads and the limit
- *            on TP".
+ *            on TP", "The cost of communication", "Exercises".
  *   [LEDGER] "8. How several ranks share one ledger" (mini-SGLang series):
  *            "Weights are cut by name".
  *   [CH9]    "Chapter 9 Multi-process and Tensor Parallelism"
