@@ -29,6 +29,7 @@
 // of tile i.  Decode, bound by the stream of K and V, keeps K and V of one
 // tile per stage (one more tile of loads in flight).
 #include "common.h"
+#include "qkv_finish.h"
 
 namespace tps {
 
@@ -117,7 +118,48 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
 
   // Q^T operands: lane supplies q[row lr, ks*16 + lh*8 .. +8]
   bf16x8 qf[8];
-  {
+  if (decode && a.qkv_splits > 0) {
+    // The projection arrives as split-K partials: sum them (split order) for
+    // this block's rep q heads and its kv head, apply QK-norm and RoPE at
+    // position past, append k and v to the caches there, and keep q on chip
+    // (staged in LDS, which the rings reuse afterwards).
+    const int n_qkv = (a.lq + 2 * a.lkv) * 128;
+    const int64_t plane = (int64_t)a.B * n_qkv;
+    const float* prow = a.qkv_part + (int64_t)b * n_qkv;
+    bf16* qs = reinterpret_cast<bf16*>(smem);          // [rep][128]
+    const int j16 = tid & 15;
+    const RopeCoef rc = rope_coef(a.theta, j16);
+    for (int u = tid >> 4; u < rep + 2; u += NT / 16) {   // a unit: 16 lanes, one head row
+      const int col = u < rep ? (head0 + u) * 128 : (u == rep ? a.lq + kvh : a.lq + a.lkv + kvh) * 128;
+      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+      for (int z = 0; z < a.qkv_splits; ++z) {
+        const float* src = prow + z * plane + col + 4 * j16;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(src), p1 = *reinterpret_cast<const f32x4*>(src + 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] += p0[e];
+          v1[e] += p1[e];
+        }
+      }
+      float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      if (u <= rep) qk_norm_rope(x, u < rep ? a.q_norm_w : a.k_norm_w, a.past, j16, rc, a.eps);
+      if (u < rep) {
+        store_head_lanes(qs + u * 128, x, j16);
+        if (a.q_store) store_head_lanes(a.q_store + (int64_t)b * ldq + (int64_t)(head0 + u) * 128, x, j16);
+      } else {
+        bf16* cache = const_cast<bf16*>(u == rep ? a.k_cache : a.v_cache);
+        store_head_lanes(cache + (((int64_t)b * a.lkv + kvh) * a.S_max + a.past) * 128, x, j16);
+      }
+    }
+    // the cache rows are complete in L2 before any wave loads its tiles
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qs + lr * 128 + ks * 16 + lh * 8) : bf16x8{};
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staging is read before the rings refill it
+    __syncthreads();
+  } else {
     const bf16* qp = decode ? a.q + (int64_t)b * ldq + (int64_t)(head0 + (row_ok ? lr : 0)) * 128
                             : a.q + ((int64_t)b * a.T + (row_ok ? t0 + lr : 0)) * ldq + (int64_t)head0 * 128;
 #pragma unroll

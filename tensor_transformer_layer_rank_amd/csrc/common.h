@@ -172,6 +172,16 @@ struct AttnArgs {
   const bf16* v_cache;
   bf16* out;             // [B*T, lq*128]
   int B, T, past, S_max, lq, lkv;
+  // Decode only, optional: the QKV projection as split-K fp32 partials
+  // [qkv_splits, B, (lq + 2 lkv) * 128] still to be summed and finished
+  // (QK-norm, RoPE, k / v appended at position past; q kept on chip and,
+  // when q_store is set, also written there).  q is then not read.
+  const float* qkv_part;
+  int qkv_splits;
+  const bf16* q_norm_w;
+  const bf16* k_norm_w;
+  float eps, theta;
+  bf16* q_store;
 };
 // Prefill kernel whose workgroups each cover a (kv head, row block) with all
 // its q heads; used when those workgroups alone fill the GPU.
@@ -180,6 +190,12 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 // One-pass flash attention for decode (rows = the q heads of a kv head) and
 // for the prefills that attn_prefill would leave the GPU short of work.
 hipError_t attn_flash(const AttnArgs& a, hipStream_t s);
+// The merged QKV projection (EPI_QKV).  With defer set and a split-K plan,
+// only the fp32 partials [splits, M, N] are written to scratch and
+// *splits_out > 0: the decode attention finishes them (AttnArgs.qkv_part).
+// Otherwise the projection is finished here and *splits_out = 0.
+hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, bool defer, int* splits_out,
+                    hipStream_t s);
 
 // --- greedy argmax over vocab-parallel logits ------------------------------
 // out_val[m], out_idx[m] = the best of the n candidates cand[m, 0:n] (8 bytes

@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "qkv_finish.h"
 
 namespace tps {
 
@@ -60,69 +61,14 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-// ---- merged QKV finish ("Tensor parallelism from scratch", "Implementation",
-// TPAttention.forward: QK-norm per head, RoPE at the absolute position, cache
-// append).  Norm: v / sqrt(mean(v^2) + eps) * w; RoPE: rotate-half, the pair
-// (v[i], v[i+64]) turns by pos * theta^(-2i/128) (Qwen3 conventions, which
-// the pages import without printing).
-//
-// 16 lanes hold one (row, head): lane j has d = 4j .. 4j+3 and their RoPE
-// partners d + 64, so the rotation stays inside the lane and the norm is a
-// 16-lane reduction.  rope_coef() gives theta^(-2i/128) / (2 pi) for the
-// lane's four indices i = 4j + e as a float head plus tail; rope_sincos()
-// forms the angle in revolutions, pos * coef, without losing the fraction
-// (the head product's rounding error by FMA, the integer part dropped before
-// the small terms are added; positions are exact in fp32 below 2^24), and
-// the hardware sine and cosine take revolutions.
-struct RopeCoef {
-  float hi[4], lo[4];
-};
-__device__ __forceinline__ RopeCoef rope_coef(float theta, int j) {
-  RopeCoef c;
-  const double l2t = log2((double)theta);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const double cr = exp2(-(double)(2 * (4 * j + e)) / 128.0 * l2t) * 0.159154943091895335768883;
-    c.hi[e] = (float)cr;
-    c.lo[e] = (float)(cr - (double)c.hi[e]);
-  }
-  return c;
-}
-__device__ __forceinline__ void rope_sincos(int pos, float hi, float lo, float& sn, float& cs) {
-  const float p = (float)pos;
-  const float q = p * hi;
-  const float err = __builtin_fmaf(p, hi, -q);   // q + err == p * hi exactly
-  const float rev = (q - __builtin_rintf(q)) + __builtin_fmaf(p, lo, err);
-  sn = __builtin_amdgcn_sinf(rev);
-  cs = __builtin_amdgcn_cosf(rev);
-}
+// ---- merged QKV finish: QK-norm and RoPE per (row, head) in qkv_finish.h;
+// here the store of q, or the append of k / v to the caches.
 // x[0..3] hold d = 4j .. 4j+3 of (row m, head h), x[4..7] hold d + 64
 __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
                                            const RopeCoef& rc) {
   const int b = (int)(m / a.T), t = (int)(m - (int64_t)b * a.T);
   const int pos = a.past + t;
-  if (h < a.lq + a.lkv) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-    ss = row_sum16(ss);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
-    const bf16* wp = (h < a.lq ? a.q_norm_w : a.k_norm_w) + 4 * j;
-    const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(wp), w1 = *reinterpret_cast<const bf16x4*>(wp + 64);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] *= inv * bf2f(w0[e]);
-      x[4 + e] *= inv * bf2f(w1[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float sn, cs;
-      rope_sincos(pos, rc.hi[e], rc.lo[e], sn, cs);
-      const float x1 = x[e], x2 = x[4 + e];
-      x[e] = x1 * cs - x2 * sn;
-      x[4 + e] = x2 * cs + x1 * sn;
-    }
-  }
+  if (h < a.lq + a.lkv) qk_norm_rope(x, h < a.lq ? a.q_norm_w : a.k_norm_w, pos, j, rc, a.eps);
   bf16* dst;
   if (h < a.lq)
     dst = a.q_out + m * ((int64_t)a.lq * 128) + (int64_t)h * 128;
@@ -130,10 +76,7 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
     dst = a.k_cache + (((int64_t)b * a.lkv + (h - a.lq)) * a.S_max + pos) * 128;
   else
     dst = a.v_cache + (((int64_t)b * a.lkv + (h - a.lq - a.lkv)) * a.S_max + pos) * 128;
-  const bf16x4 o0 = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
-  const bf16x4 o1 = {f2bf(x[4]), f2bf(x[5]), f2bf(x[6]), f2bf(x[7])};
-  *reinterpret_cast<bf16x4*>(dst + 4 * j) = o0;
-  *reinterpret_cast<bf16x4*>(dst + 64 + 4 * j) = o1;
+  store_head_lanes(dst, x, j);
 }
 // the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
 constexpr bool qkv_tile_ok(int bm, int bn, int stages, int bk = 64) {
@@ -1038,8 +981,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split) {
   return best;
 }
 
+// finish = false: a split plan stops after the partials (the consumer sums
+// them itself)
 template <int BM, int BN, int WGM, int WGN, int S>
-hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s) {
+hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s,
+                       bool finish = true) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int GM = 8;
   if (pl.splits > 1) {
@@ -1048,6 +994,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     q.ldc = p.N;
     dim3 grid(pl.tiles_m * pl.tiles_n, pl.splits);
     gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
+    if (!finish) return hipGetLastError();
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
     int64_t g = (p.M * (cols / 4) + 255) / 256;
     if (g > 4096) g = 4096;
@@ -1150,6 +1097,26 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
     case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s);
     case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s);
     default: return launch_tile<64, 64, 2, 2, 8>(p, epi, pl, scratch, s);
+  }
+}
+
+hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, bool defer, int* splits_out,
+                    hipStream_t s) {
+  *splits_out = 0;
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  const bool can_split = scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, EPI_QKV);
+  const Plan pl = make_plan(p.M, p.N, p.K, EPI_QKV, can_split);
+  if (!defer || pl.splits == 1) return gemm_bf16(p, EPI_QKV, scratch, scratch_bytes, s);
+  *splits_out = pl.splits;
+  switch (pl.v) {
+    case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, false);
+    case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, EPI_QKV, pl, scratch, s, false);
+    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, EPI_QKV, pl, scratch, s, false);
+    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, false);
+    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, false);
+    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, false);
+    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, false);
+    default: return launch_tile<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, false);
   }
 }
 

@@ -255,11 +255,23 @@ int tp_qkv_attn(const tp_cfg* cfg, const void* x, int32_t B, int32_t T, int32_t 
   g.qkv = QkvArgs{static_cast<const bf16*>(q_norm_w), static_cast<const bf16*>(k_norm_w), q,
                   static_cast<bf16*>(k_cache), static_cast<bf16*>(v_cache), B, T, past_len, S_max, L.lq, L.lkv,
                   cfg->rms_eps, cfg->rope_theta};
-  hipError_t e = gemm_bf16(g, EPI_QKV, scratch, w.scratch_bytes, s);
+  //    (decode with a split-K plan: only the partials; the attention kernel
+  //    finishes them, which saves the reduction launch)
+  int qkv_splits = 0;
+  hipError_t e = gemm_qkv(g, scratch, w.scratch_bytes, T == 1, &qkv_splits, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
   // 2. attention over the local heads
   AttnArgs aa{q, static_cast<const bf16*>(k_cache), static_cast<const bf16*>(v_cache), attn,
               B, T, past_len, S_max, L.lq, L.lkv};
+  if (qkv_splits > 0) {
+    aa.qkv_part = static_cast<const float*>(scratch);
+    aa.qkv_splits = qkv_splits;
+    aa.q_norm_w = static_cast<const bf16*>(q_norm_w);
+    aa.k_norm_w = static_cast<const bf16*>(k_norm_w);
+    aa.eps = cfg->rms_eps;
+    aa.theta = cfg->rope_theta;
+    aa.q_store = q_out_opt ? q : nullptr;
+  }
   e = T > 1 && attn_prefill_fills(B, T, L.lq, L.lkv) ? attn_prefill(aa, s) : attn_flash(aa, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
   // 3. row-parallel o_proj -> partial sum
