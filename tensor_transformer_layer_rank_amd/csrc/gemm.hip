@@ -14,6 +14,8 @@
 // contiguous, M-grouped range of tiles and shares A/B panels in its own L2.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "qkv_finish.h"
 
@@ -928,8 +930,10 @@ constexpr double kEpiUsPerKB = 0.03;           // tile write-out per resident ro
 
 struct Plan { int v; int splits; int64_t kps; int tiles_m, tiles_n; };
 
+// consumer_sums: the split partials are summed by the next kernel, so a
+// split costs their traffic but no reduction launch
 double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int64_t splits, int64_t* tm_out,
-                 int64_t* tn_out) {
+                 int64_t* tn_out, bool consumer_sums = false) {
   const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;
   const int64_t bn_out = epi == EPI_SILU_BF16 && splits == 1 ? v.bn / 2 : v.bn;
   const int64_t cols = splits == 1 ? ncols : N;   // split partials use the plain column order
@@ -952,11 +956,13 @@ double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int
   const double t_mem = wgs >= kCUs ? bytes / rate
                                    : bytes / rate * ((double)rounds * resident / (wgs > resident ? wgs : resident));
   // the reduction runs after the GEMM: it reads every partial and writes C
-  const double t_red = splits > 1 ? (partial + (double)M * ncols * (epi == EPI_F32 ? 4 : 2)) / kHbmBytesPerUs + kReduceUs : 0.0;
+  const double t_red = splits <= 1 ? 0.0
+                      : consumer_sums ? partial / kHbmBytesPerUs
+                                      : (partial + (double)M * ncols * (epi == EPI_F32 ? 4 : 2)) / kHbmBytesPerUs + kReduceUs;
   return (t_comp > t_mem ? t_comp : t_mem) + kLaunchUs + t_red;
 }
 
-Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split) {
+Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool consumer_sums = false) {
   Plan best{V256x256, 1, K, 0, 0};
   double best_cost = 1e300;
   const int64_t kblocks = (K + 63) / 64;
@@ -970,7 +976,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split) {
       if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
-      const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn) * (sp > 1 ? 1.05 : 1.0);
+      const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn, consumer_sums) * (sp > 1 ? 1.05 : 1.0);
       if (c < best_cost * 0.999) {
         best_cost = c;
         const int64_t kps = sp == 1 ? K : ((kblocks + sp - 1) / sp) * 64;
@@ -1068,8 +1074,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int epi) {
   if (M <= 0 || N <= 0 || epi == EPI_ARGMAX) return 0;
-  const Plan pl = make_plan(M, N, K, epi, true);
-  return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+  int64_t splits = make_plan(M, N, K, epi, true).splits;
+  // the QKV projection may also run with its partials summed by the decode
+  // attention, which can prefer more splits
+  if (epi == EPI_QKV) splits = std::max<int64_t>(splits, make_plan(M, N, K, epi, true, true).splits);
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
 int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
@@ -1104,19 +1113,22 @@ hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, b
                     hipStream_t s) {
   *splits_out = 0;
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const bool can_split = scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, EPI_QKV);
-  const Plan pl = make_plan(p.M, p.N, p.K, EPI_QKV, can_split);
-  if (!defer || pl.splits == 1) return gemm_bf16(p, EPI_QKV, scratch, scratch_bytes, s);
-  *splits_out = pl.splits;
+  if (!defer) return gemm_bf16(p, EPI_QKV, scratch, scratch_bytes, s);
+  Plan pl = make_plan(p.M, p.N, p.K, EPI_QKV, scratch != nullptr, true);
+  if (pl.splits > 1 && scratch_bytes < (size_t)pl.splits * p.M * p.N * sizeof(float))
+    pl = make_plan(p.M, p.N, p.K, EPI_QKV, false, true);   // no room for the partials
+  const bool split = pl.splits > 1;
+  if (split) *splits_out = pl.splits;
+  // unsplit: the tile finishes its heads in the epilogue as usual
   switch (pl.v) {
-    case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, false);
-    case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, EPI_QKV, pl, scratch, s, false);
-    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, EPI_QKV, pl, scratch, s, false);
-    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, false);
-    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, false);
-    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, false);
-    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, false);
-    default: return launch_tile<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, false);
+    case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, !split);
+    case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, !split);
+    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
+    default: return launch_tile<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, !split);
   }
 }
 
