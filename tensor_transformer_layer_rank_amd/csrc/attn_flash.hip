@@ -225,6 +225,22 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   auto soft_pv = [&](f32x16 s, int kt, int st) {
     const unsigned char* V = ring + st * kStageB + kTileB;
     const int key0 = kt * kKeys;
+    // V^T operands do not depend on P: their transposing reads go out first
+    // and land while the VALU does the softmax
+    bf16x8 vf[4][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int key = sub * 16 + tr_key;
+        const int d = db * 32 + tr_d;
+        const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
+        const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+        const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
+        const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
+        vf[db][sub] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      }
+    __builtin_amdgcn_sched_barrier(0);
     // raw max over this tile's visible scores (the scale is positive)
     float mx = -INFINITY;
     if (key0 + kKeys - 1 > min_pos) {                      // some key may follow some row
@@ -264,16 +280,7 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int key = sub * 16 + tr_key;
-        const int d = db * 32 + tr_d;
-        const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
-        const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
-        const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
-        const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
-        const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sub], o[db], 0, 0, 0);
-      }
+      for (int sub = 0; sub < 2; ++sub) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][sub], pf[sub], o[db], 0, 0, 0);
   };
 
   const int n = w1 - w0;
