@@ -198,6 +198,24 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
       }
     const int key0 = kt * kKeys;
     const bool diag = key0 + kKeys - 1 > a.past + t0w;     // some key may follow some row
+    // V^T operands do not depend on P: their transposing reads go out first
+    // and land while the VALU does the softmax
+    bf16x8 vf[4][2][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int key = kb * 32 + sub * 16 + tr_key;
+          const int d = db * 32 + tr_d;
+          const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
+          const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+          const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
+          const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
+          vf[db][kb][sub] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[HW][4];
 #pragma unroll
     for (int hw = 0; hw < HW; ++hw) {
@@ -248,18 +266,11 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const int key = kb * 32 + sub * 16 + tr_key;
-          const int d = db * 32 + tr_d;
-          const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
-          const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
-          const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
-          const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
-          const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int hw = 0; hw < HW; ++hw)
-            o[hw][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hw][kb * 2 + sub], o[hw][db], 0, 0, 0);
-        }
+            o[hw][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][kb][sub], pf[hw][kb * 2 + sub], o[hw][db], 0,
+                                                                0, 0);
   };
 
   // ring: tiles kt0 + i live in stage i % NS; NS - 1 tiles in flight.  The
