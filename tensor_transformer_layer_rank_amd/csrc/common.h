@@ -51,12 +51,16 @@ __device__ __forceinline__ void cand_step_dpp(float& v, int& i) {
     i = oi;
   }
 }
-// best candidate of each 32-lane half of the wave, in all its lanes
-__device__ __forceinline__ void cand_best32(float& v, int& i) {
+// best candidate of each 16-lane row of the wave, in all its lanes
+__device__ __forceinline__ void cand_best16(float& v, int& i) {
   cand_step_dpp<0xB1>(v, i);    // quad_perm [1,0,3,2]
   cand_step_dpp<0x4E>(v, i);    // quad_perm [2,3,0,1]
   cand_step_dpp<0x141>(v, i);   // row_half_mirror
   cand_step_dpp<0x140>(v, i);   // row_mirror
+}
+// best candidate of each 32-lane half of the wave, in all its lanes
+__device__ __forceinline__ void cand_best32(float& v, int& i) {
+  cand_best16(v, i);
   const auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   const auto pi = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
   // each lane sees its own row's value in one output and the paired row's in
@@ -202,6 +206,14 @@ hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, b
 // each: float value, int32 column, column < 0 = none), column + idx0.
 hipError_t argmax_candidates(const void* cand, int64_t M, int64_t n, int64_t idx0, float* out_val, int32_t* out_idx,
                              hipStream_t s);
+// Decode head with the rows resident in LDS (M <= 64, K <= 1024, K % 256
+// == 0, N >= 1, N * K * 2 < 2^31): one candidate per (row, workgroup) into
+// cand [M, groups] (groups = argmax_resident_groups()), columns local to
+// the vocab slice.
+bool argmax_resident_ok(int64_t M, int64_t N, int64_t K);
+int argmax_resident_groups();
+hipError_t argmax_resident(const void* x, int64_t M, const void* vocab, int64_t N, int64_t K, void* cand,
+                           hipStream_t s);
 // out_idx[m] = the candidate (vals, idx [n_shards, M]) with the largest
 // value, ties to the smallest index, idx < 0 skipped; out_val optional.
 hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, int64_t M, int32_t* out_idx,

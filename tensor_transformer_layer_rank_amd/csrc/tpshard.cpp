@@ -96,13 +96,17 @@ MlpWs mlp_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
 }
 
 // workspace of tp_lm_head_argmax: one 8-byte candidate per row and N tile
+// of the logits GEMM, or per row and workgroup of the resident-rows kernel
 struct LmWs {
+  bool resident;
   int64_t tiles_n;
   size_t total;
 };
 LmWs lm_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
   LmWs w{};
-  w.tiles_n = gemm_argmax_tiles_n(M, L.vocab_end - L.vocab_start, c->hidden);
+  const int64_t N = L.vocab_end - L.vocab_start;
+  w.resident = argmax_resident_ok(M, N, c->hidden);
+  w.tiles_n = w.resident ? argmax_resident_groups() : gemm_argmax_tiles_n(M, N, c->hidden);
   w.total = align_up((size_t)(M * w.tiles_n) * 8);
   return w;
 }
@@ -357,7 +361,11 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* v
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t N = L.vocab_end - L.vocab_start, H = cfg->hidden;
-  if (N > 0) {
+  if (w.resident) {
+    // few rows, short hidden size: rows resident in LDS, the vocab slice
+    // streamed once
+    if (argmax_resident(x, M, vocab_local, N, H, workspace, s) != hipSuccess) return TP_ERR_LAUNCH;
+  } else if (N > 0) {
     // logits GEMM whose epilogue leaves one candidate per row and N tile
     GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), workspace, M, N, H, H, H,
                   w.tiles_n, 0};

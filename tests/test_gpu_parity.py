@@ -549,18 +549,25 @@ def test_lm_head_argmax_decode_full_vocab():
     assert np.array_equal(ri, np.argmax(full, axis=1))
 
 
-@pytest.mark.parametrize("case", ["ragged-ties", "empty-shard"])
+@pytest.mark.parametrize("case", ["ragged-ties", "empty-shard", "rows-in-lds-ties", "rows-in-lds-empty-shard",
+                                  "rows-in-lds-one-row", "rows-in-lds-h256", "rows-in-lds-m20"])
 def test_lm_head_argmax_ragged(case):
     """Odd local vocab sizes (row stride not a multiple of 16 bytes), uneven
     shards, planted exact ties across shards (the smallest id must win), and
-    an empty last shard that must never win."""
-    if case == "ragged-ties":
-        V, H, n, M = 1001, 520, 3, 37
-        out = _argmax_case(V, H, n, M, 13, ties=True)
+    an empty last shard that must never win.  The rows-in-LDS cases take the
+    resident-rows kernel (hidden a multiple of 256, up to 64 rows, in its
+    16-, 32- and 64-row forms): fewer vocab rows than waves (most waves get
+    none), one row, 20 rows, 64 rows."""
+    if case in ("ragged-ties", "rows-in-lds-ties"):
+        V, H, n, M = (1001, 520, 3, 37) if case == "ragged-ties" else (701, 256, 2, 37)
+        out = _argmax_case(V, H, n, M, 13 if case == "ragged-ties" else 15, ties=True)
         assert (out[7][0::4] == 3).all()           # the oracle's winner is the first copy
     else:
-        V, H, n, M = 5, 64, 4, 9
-        out = _argmax_case(V, H, n, M, 14)
+        V, H, n, M, wid = {"empty-shard": (5, 64, 4, 9, 14), "rows-in-lds-empty-shard": (5, 256, 4, 9, 18),
+                           "rows-in-lds-one-row": (151936, 1024, 2, 1, 16),
+                           "rows-in-lds-h256": (5003, 256, 3, 64, 17),
+                           "rows-in-lds-m20": (30011, 512, 2, 20, 19)}[case]
+        out = _argmax_case(V, H, n, M, wid)
     gvr, gir, gv, gi, ov, oi, rv, ri, xc, Ec = out
     for r in range(n):
         if oi[r][0] < 0:
