@@ -6,10 +6,12 @@
 // it), and the candidates of all ranks combine to the max, ties to the
 // smaller global index -- the first maximum of the concatenated logits.
 //
-// The logits GEMM reduces each tile row to a candidate in its epilogue
-// (EPI_ARGMAX in gemm.hip), so the logits never reach memory.
-// argmax_pairs: one workgroup per row reduces the row's tile candidates
-// (a per-thread best, then wave shuffles and LDS).  combine_candidates: one
+// The logits never reach memory.  Up to 64 rows with a hidden size of at
+// most 1024 go to argmax_resident_kernel (below: rows resident in LDS, the
+// vocab slice streamed once); other shapes to the logits GEMM, which reduces
+// each tile row to a candidate in its epilogue (EPI_ARGMAX in gemm.hip).
+// argmax_pairs: one workgroup per row reduces the row's candidates (a
+// per-thread best, then wave shuffles and LDS).  combine_candidates: one
 // thread per row over the ranks.
 #include "common.h"
 
