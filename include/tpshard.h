@@ -9,8 +9,8 @@
  *   - GQA attention over the rank's local heads (kv heads replicated when the
  *     tensor-parallel size exceeds the kv-head count),
  *   - the vocab-parallel masked embedding and the lm_head vocab slice,
- *   - the greedy decode head: per-shard (max, first id) candidates fused into
- *     the logits GEMM, and their combine across shards,
+ *   - the greedy decode head: per-shard (max, first id) candidates computed
+ *     without storing the logits, and their combine across shards,
  *   - the residual add of the summed row-parallel partials with the next
  *     RMSNorm, and its sequence-parallel form on the rank's token slice.
  *
@@ -220,8 +220,11 @@ int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_lo
  * (gathered into [n_shards, M]) combine with tp_argmax_combine.
  * x: bf16 [M, H]; vocab_local: bf16 [vocab_end - vocab_start, H];
  * out_val: float [M]; out_idx: int32 [M];
- * workspace >= tp_workspace_bytes(cfg, TP_OP_LM_ARGMAX, M, 1, 0) (it holds the
- * local logits).  Requires TP_BF16 (TP_ERR_DTYPE) and H % 8 == 0.  M = 0: no-op. */
+ * workspace >= tp_workspace_bytes(cfg, TP_OP_LM_ARGMAX, M, 1, 0), 16-byte
+ * aligned: it holds 8-byte partial candidates (per row and logits tile, or per
+ * row and workgroup when up to 64 rows with H <= 1024, H % 256 == 0 keep x
+ * resident on chip); the logits themselves are never stored.  Requires
+ * TP_BF16 (TP_ERR_DTYPE) and H % 8 == 0.  M = 0: no-op. */
 int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local,
                       float* out_val, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
 
