@@ -193,6 +193,21 @@ def test_lm_head_argmax_and_combine_validation():
     assert _status(tp.tp_argmax_combine, A, Fake((1 << 40) + 2, 5), 2, 5, A, None, s) == E_ALIGN
 
 
+def test_lm_head_argmax_workspace_paths():
+    """The decode head's workspace holds 8-byte candidates: one per row and
+    workgroup (256 of them) when up to 64 rows with a hidden size of at most
+    1024 (a multiple of 256) keep the activations on chip, else one per row
+    and logits tile.  Host logic only."""
+    c = tp.Cfg(hidden=1024, vocab=151936, tp_size=2)
+    for M in (1, 16, 33, 64):
+        assert tp.tp_workspace_bytes(c, tp.TP_OP_LM_ARGMAX, M, 1) == M * 256 * 8
+    for cfg, M in ((c, 65), (tp.Cfg(hidden=520, vocab=151936, tp_size=2), 8),
+                   (tp.Cfg(hidden=5120, vocab=151936, tp_size=2), 8)):
+        need = tp.tp_workspace_bytes(cfg, tp.TP_OP_LM_ARGMAX, M, 1)
+        assert need >= M * 8 and need % 16 == 0
+        assert need != M * 256 * 8                                  # the logits-GEMM path
+
+
 def test_residual_rmsnorm_validation():
     s = NullStream()
     c = tp.Cfg(hidden=256, tp_size=2)
