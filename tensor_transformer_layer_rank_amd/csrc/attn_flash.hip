@@ -14,7 +14,7 @@
 // Its four waves split the block's key range into four contiguous parts.
 // Each wave streams its part through a private ring of two LDS stages
 // (32-key K and V tiles, direct global->LDS buffer loads, 16-byte chunks of
-// a key row XOR-swizzled by the key so that operand reads avoid bank
+// a key row XOR-swizzled by a rotation of the key so that operand reads avoid bank
 // conflicts) and keeps an online softmax in the exp2 domain:
 //  * S^T[32 keys, 32 q] = K . Q^T with Q^T in VGPRs: each lane column is one
 //    query row, so its max and sum are lane-local plus one exchange with the
@@ -48,7 +48,12 @@ constexpr float kSlack = 8.f;                 // lazy-rescale margin, log2 units
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // byte offset of 16-byte chunk c (d = 8c .. 8c+7) of key row `key` in a tile
-__device__ __forceinline__ uint32_t toff(int key, int c) { return (uint32_t)(key * 256 + ((c ^ (key & 15)) << 4)); }
+// Key row swizzle: a rotation of the key's low four bits.  The transposing
+// V reads take 4 consecutive keys x 4 chunks per 32 lanes and the K reads 16
+// consecutive keys x 1 chunk; both land on distinct banks (plain key & 15
+// maps keys k and k ^ 1 onto the same pair of chunks: 2-way conflicts).
+__device__ __forceinline__ int kswz(int key) { return ((key << 2) | ((key >> 2) & 3)) & 15; }
+__device__ __forceinline__ uint32_t toff(int key, int c) { return (uint32_t)(key * 256 + ((c ^ kswz(key)) << 4)); }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
@@ -189,7 +194,7 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int key = 4 * i + (lane >> 4);
-      const uint32_t sw = (uint32_t)(((lane & 15) ^ (key & 15)) << 4);
+      const uint32_t sw = (uint32_t)(((lane & 15) ^ kswz(key)) << 4);
       dma16(rk, (uint32_t)(kt * kKeys + key) * 256u + sw, base + i * 1024);
       dma16(rv, (uint32_t)(vt * kKeys + key) * 256u + sw, base + kTileB + i * 1024);
     }

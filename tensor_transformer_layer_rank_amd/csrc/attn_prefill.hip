@@ -9,7 +9,7 @@
 //    GQA, else 1), so every K or V operand it reads from LDS feeds HW MFMAs;
 //  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads
 //    with the lds flag) through a ring of NS stages; 16-byte chunks of a key
-//    row are XOR-swizzled by the key so that operand reads avoid bank
+//    row are XOR-swizzled by a rotation of the key so that operand reads avoid bank
 //    conflicts;
 //  * S^T[64 keys, 32 q] = K . Q^T with Q^T held in VGPRs: each lane column
 //    is one query, so its row max and sum are lane-local plus one exchange
@@ -41,7 +41,12 @@ constexpr float kSlack = 8.f;                 // lazy-rescale margin, log2 units
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // byte offset of 16-byte chunk c (d = 8c .. 8c+7) of key row `key` in a tile
-__device__ __forceinline__ uint32_t toff(int key, int c) { return (uint32_t)(key * 256 + ((c ^ (key & 15)) << 4)); }
+// Key row swizzle: a rotation of the key's low four bits.  The transposing
+// V reads take 4 consecutive keys x 4 chunks per 32 lanes and the K reads 16
+// consecutive keys x 1 chunk; both land on distinct banks (plain key & 15
+// maps keys k and k ^ 1 onto the same pair of chunks: 2-way conflicts).
+__device__ __forceinline__ int kswz(int key) { return ((key << 2) | ((key >> 2) & 3)) & 15; }
+__device__ __forceinline__ uint32_t toff(int key, int c) { return (uint32_t)(key * 256 + ((c ^ kswz(key)) << 4)); }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
@@ -152,7 +157,7 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
     for (int j = 0; j < 4; ++j) {
       const int i = wave * 4 + j;
       const int key = 4 * i + (lane >> 4);
-      const uint32_t off = (uint32_t)(kt * kKeys + key) * 256u + (uint32_t)(((lane & 15) ^ (key & 15)) << 4);
+      const uint32_t off = (uint32_t)(kt * kKeys + key) * 256u + (uint32_t)(((lane & 15) ^ kswz(key)) << 4);
       dma16(rk, off, base + i * 1024);
       dma16(rv, off, base + kTile + i * 1024);
     }
