@@ -549,6 +549,73 @@ def test_lm_head_argmax_decode_full_vocab():
     assert np.array_equal(ri, np.argmax(full, axis=1))
 
 
+_BIG_VOCAB = {}
+
+
+def _big_vocab(V, H):
+    """One synthetic full vocabulary [V, H] (bf16, N(0, 0.02)) shared by the
+    full-size decode-head cases."""
+    if (V, H) not in _BIG_VOCAB:
+        _BIG_VOCAB.clear()
+        _BIG_VOCAB[(V, H)] = synth.embedding(4, V, H)
+    return _BIG_VOCAB[(V, H)]
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_lm_head_argmax_full_size_sampled(wid):
+    """The 32B decode heads at full size in the bench's launch configuration
+    (hidden 5120: the logits-GEMM path with the argmax epilogue; 128 decode
+    rows over 2 ranks, 256 over 16): every rank's shard runs, the ranks'
+    candidates are combined on the GPU, and sampled rows are checked against
+    the oracle over each rank's whole vocab slice and over the whole
+    vocabulary."""
+    w = synth.WORKLOADS[wid]
+    V, H, n, M = w["vocab"], w["hidden"], w["tp"], w["decode_B"]
+    E = _big_vocab(V, H)
+    x = synth.activations(wid, M, H)
+    Eg, xg = E.to(DEV), x.to(DEV)
+    vals = torch.empty(n, M, dtype=torch.float32, device=DEV)
+    idx = torch.empty(n, M, dtype=torch.int32, device=DEV)
+    ranges = []
+    for r in range(n):
+        c = tp.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        L = tp.tp_local_dims(c)
+        ranges.append((L.vocab_start, L.vocab_end))
+        shard = torch.empty(L.vocab_end - L.vocab_start, H, dtype=torch.bfloat16, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_VOCAB, Eg, shard)
+        ws = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_LM_ARGMAX, M, 1), dtype=torch.uint8, device=DEV)
+        tp.tp_lm_head_argmax(c, xg, M, shard, vals[r], idx[r], ws)
+        del shard
+    out_i = torch.empty(M, dtype=torch.int32, device=DEV)
+    out_v = torch.empty(M, dtype=torch.float32, device=DEV)
+    tp.tp_argmax_combine(vals, idx, n, M, out_i, out_v)
+    torch.cuda.synchronize()
+    del Eg
+    gvr, gir = vals.cpu().numpy(), idx.cpu().numpy()
+    gv, gi = out_v.cpu().numpy(), out_i.cpu().numpy()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M + wid).integers(0, M, 4)]))
+    xc = synth.to_f64(x)[rows]
+    ov, oi = [], []
+    for r, (a, b) in enumerate(ranges):
+        v, i = O.lm_head_argmax(xc, synth.to_f64(E[a:b]), a)
+        ov.append(v)
+        oi.append(i)
+    rv, ri = O.argmax_combine(np.stack(ov), np.stack(oi))
+
+    def check(got_v, got_i, ref_v, ref_i):
+        # as _check_argmax, with the chosen id's logit taken from E directly
+        for k, m in enumerate(rows):
+            if got_i[m] == ref_i[k]:
+                assert got_v[m] == ref_v[k], (wid, m, got_v[m], ref_v[k])
+                continue
+            logit = O.bf16(xc[k] @ synth.to_f64(E[int(got_i[m])]))
+            assert abs(logit - ref_v[k]) <= 2.0 ** -7 * abs(ref_v[k]), (wid, m, got_i[m], ref_i[k])
+
+    for r in range(n):
+        check(gvr[r], gir[r], ov[r], oi[r])
+    check(gv, gi, rv, ri)
+
+
 @pytest.mark.parametrize("case", ["ragged-ties", "empty-shard", "rows-in-lds-ties", "rows-in-lds-empty-shard",
                                   "rows-in-lds-one-row", "rows-in-lds-h256", "rows-in-lds-m20"])
 def test_lm_head_argmax_ragged(case):
