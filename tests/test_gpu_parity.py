@@ -201,8 +201,12 @@ def test_embed_vocab_bit_exact_and_vocab_sum(case):
 
 # ------------------------------------------------------------------ lm_head
 
-@pytest.mark.parametrize("case", ["w3", "mid", "many-ragged"])
+@pytest.mark.parametrize("case", ["w3", "w4-32b-tp2", "w5-32b-tp16", "mid", "many-ragged"])
 def test_lm_head(case):
+    """Logits of a vocab shard.  w3 and the 32B cases are the bench's lm_head
+    shapes at full size (4096 rows at tp=2 and 1024 rows at tp=16 of the 32B
+    hidden size 5120: the persistent kernel over 80 K blocks), sampled rows
+    against the oracle."""
     if case == "w3":
         w = synth.WORKLOADS[3]
         V, H, n, M = w["vocab"], w["hidden"], w["tp"], w["n_ids"]
@@ -210,6 +214,14 @@ def test_lm_head(case):
         x = synth.activations(3, M, H)
         rows = np.unique(np.concatenate([[0, 1, M - 1], np.random.default_rng(3).integers(0, M, 13)]))
         ranks = [0, 1]
+    elif case in ("w4-32b-tp2", "w5-32b-tp16"):
+        wid = 4 if case.startswith("w4") else 5
+        w = synth.WORKLOADS[wid]
+        V, H, n, M = w["vocab"], w["hidden"], w["tp"], 4096 if wid == 4 else 1024
+        E = _big_vocab(V, H)
+        x = synth.activations(wid, M, H)
+        rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(wid).integers(0, M, 8)]))
+        ranks = [0]
     elif case == "many-ragged":
         # over eight rounds of 256 x 256 tiles (the persistent kernel), with
         # ragged M, N and K tails
@@ -234,7 +246,7 @@ def test_lm_head(case):
         logits = torch.empty(M, L.vocab_end - L.vocab_start, dtype=torch.bfloat16, device=DEV)
         tp.tp_lm_head(c, xg, M, shard, logits)
         torch.cuda.synchronize()
-        ref = O.lm_head(synth.to_f64(x)[rows], synth.to_f64(E)[L.vocab_start:L.vocab_end])
+        ref = O.lm_head(synth.to_f64(x)[rows], synth.to_f64(E[L.vocab_start:L.vocab_end]))
         err = relerr(f64(logits)[rows], ref)
         assert err <= TOL_BF16, (case, r, err)
 
