@@ -167,13 +167,22 @@ def test_shard_weights_fp32_and_vocab():
         assert np.array_equal(bits16(dst), ref)
 
 
-@pytest.mark.parametrize("case", ["w3", "ragged"])
+@pytest.mark.parametrize("case", ["w3", "w4-32b-tp2", "w5-32b-tp16", "ragged"])
 def test_embed_vocab_bit_exact_and_vocab_sum(case):
+    """Masked embedding on every rank, bit-exact, and the ranks' outputs sum
+    to the full table's rows.  w3 and the 32B cases are the bench's embed
+    shapes at full size (4096 or 1024 ids over the 151936-row vocabulary)."""
     if case == "w3":
         w = synth.WORKLOADS[3]
         V, H, n, n_ids = w["vocab"], w["hidden"], w["tp"], w["n_ids"]
         E = synth.embedding(3, V, H)
         ids = synth.token_ids(3, n_ids, V)
+    elif case in ("w4-32b-tp2", "w5-32b-tp16"):
+        wid = 4 if case.startswith("w4") else 5
+        w = synth.WORKLOADS[wid]
+        V, H, n = w["vocab"], w["hidden"], w["tp"]
+        E = _big_vocab(V, H)
+        ids = synth.token_ids(wid, 4096 if wid == 4 else 1024, V)
     else:
         V, H, n = 1001, 72, 3
         E = synth.embedding(9, V, H)
