@@ -13,6 +13,8 @@
 // argmax_pairs: one workgroup per row reduces the row's candidates (a
 // per-thread best, then wave shuffles and LDS).  combine_candidates: one
 // thread per row over the ranks.
+#include <type_traits>
+
 #include "common.h"
 
 namespace tps {
@@ -84,157 +86,116 @@ __global__ __launch_bounds__(256) void combine_candidates(const float* __restric
   }
 }
 
-// ---- decode head with the rows resident in LDS ---------------------------
-// For a few rows and a short hidden size (M <= 64, K <= 1024, K % 256 == 0)
-// the rows fit in LDS (at most 128 KB), so every workgroup keeps them for
-// the whole launch and each wave streams a contiguous run of whole 16-row
-// chunks of the vocab slice straight from memory into MFMA registers: the
-// slice is read once, the activations once per workgroup.  16x16x32
-// products, so one load instruction reads 16 vocab rows x 64 contiguous
-// bytes.  Per lane the best (value, column) of each row is kept across the
-// run; lanes and waves combine at the end into one candidate per
-// (row, workgroup).  Values compare as the bf16-rounded logits, as in the
-// GEMM epilogue.
-// NW: waves per workgroup; NB: operand buffers (NB - 1 steps of loads in
-// flight while one computes); MQ: 16-row groups of the activations.  A step
-// is 8 k-steps of 32 (256 of K).
-constexpr int kResSegK = 256;
+// ---- decode head with the rows resident on chip ---------------------------
+// For a few rows and a short hidden size (M <= 64, K = 256, 512, 768 or
+// 1024) the activations stay on chip for the whole launch and the vocab slice
+// is streamed once, straight into MFMA registers (16x16x32 products: one load
+// instruction reads 16 vocab rows x 64 contiguous bytes); no logits tile is
+// staged.  A workgroup (one per CU) runs a contiguous run of whole 16-row
+// vocab chunks; its four waves split K into quarters, so each wave keeps its
+// quarter of the rows (MQ 16-row groups x KS k-steps of 32) in VGPRs, and all
+// four work on the same chunk.  Their partial products meet in LDS
+// (double-buffered, one barrier per chunk); wave w then sums the four
+// partials of row group w in K order -- the MFMA output layout, so lane
+// (l16, g) owns rows 16w + 4g + e at chunk column l16 -- and keeps the
+// running best (value, column) of the bf16-rounded logits, as the GEMM
+// epilogue compares them.  At the end each row's 16 column slots reduce to
+// one candidate per (row, workgroup).
+// The loads are unconditional: past the run (and past N) their offsets fall
+// outside the descriptors' ranges and load zeros without a memory access,
+// so no branch disturbs the compiler's wait counts; a scheduling barrier
+// after each chunk's loads keeps chunks in issue order.
+constexpr int kResSegK = 256;                // K granularity of the head
 
-__device__ __forceinline__ int res_swz(int row, int chunk) { return chunk ^ (row & 15); }
-
-template <int NW, int NB, int MQ>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const bf16* __restrict__ vocab, int64_t N, int K,
+template <int MQ, int KS, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const bf16* __restrict__ vocab, int64_t N,
                             u32x2* __restrict__ cand) {
-  constexpr int RW = 16 * MQ;
-  __shared__ __attribute__((aligned(16))) bf16 sa[RW * 1024];  // rows x K, 16-byte chunks XOR-swizzled by row
-  __shared__ float s_v[NW][RW];
-  __shared__ int s_i[NW][RW];
+  constexpr int K = KS * 128;                 // 4 waves x KS steps x 32
+  __shared__ float red[2][4][16 * MQ][16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int kc = K / 8;                      // 16-byte chunks per row
-  // 1. the rows into LDS (rows past M as zeros), eight loads in flight per
-  // thread before their stores
-  constexpr int NT = 64 * NW, UNR = 8;
-  for (int q0 = tid; q0 < RW * kc; q0 += NT * UNR) {
-    u32x4 v[UNR];
+  const int kw0 = wave * (K / 4);             // this wave's K quarter
+  // the rows' fragments of this quarter (rows past M read as zeros)
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(x), (short)0, (int)(M * K * 2), 0x00020000);
+  bf16x8 af[KS][MQ];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int q = q0 + u * NT;
-      const int r = q / kc, p = q - r * kc;
-      v[u] = q < RW * kc && r < M ? *reinterpret_cast<const u32x4*>(x + (int64_t)r * K + res_swz(r, p) * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int q = q0 + u * NT;
-      const int r = q / kc, p = q - r * kc;
-      if (q < RW * kc) *reinterpret_cast<u32x4*>(sa + r * K + p * 8) = v[u];
-    }
-  }
-  __syncthreads();
-
-  // 2. this wave's run [r0, r0 + nrows) of whole 16-row chunks (only the last
-  // run of the slice is ragged).  One descriptor spans the slice, built from
-  // the arguments alone so that it stays in scalar registers; its range check
-  // zero-fills the rows past N, and steps past the run take an offset beyond
-  // the range, which loads zeros without a memory access.
-  const int64_t gw = (int64_t)blockIdx.x * NW + wave, nw = (int64_t)gridDim.x * NW;
+    for (int i = 0; i < MQ; ++i)
+      af[s][i] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((i * 16 + l16) * K + kw0 + s * 32 + g * 8) * 2u,
+                                                        0, 0));
+  // this workgroup's run of whole 16-row chunks
   const int64_t nch = (N + 15) / 16;
-  const int c0 = (int)(nch * gw / nw), c1 = (int)(nch * (gw + 1) / nw);
-  const int r0 = 16 * c0;
-  const int nrows = (int)min(N, (int64_t)16 * c1) - r0;
+  const int c0 = (int)(nch * blockIdx.x / gridDim.x), c1 = (int)(nch * (blockIdx.x + 1) / gridDim.x);
+  const int n = c1 - c0;
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(vocab), (short)0, (int)(N * K * 2), 0x00020000);
-  const int nseg = K / kResSegK;
-  const int steps = (c1 - c0) * nseg;         // (chunk of 16 rows, K segment)
-  float bv[MQ][4];
-  int bi[MQ][4];
-  f32x4 acc[MQ];
+  u32x4 bfr[NB][KS];
+  auto load_chunk = [&](int j, u32x4 (&b)[KS]) __attribute__((always_inline)) {
+    const uint32_t off = j < n ? (uint32_t)(((c0 + j) * 16 + l16) * K + kw0 + g * 8) * 2u : 0x80000000u;
 #pragma unroll
-  for (int i = 0; i < MQ; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      bv[i][e] = -INFINITY;
-      bi[i][e] = -1;
-      acc[i][e] = 0.f;
-    }
-  u32x4 bfr[NB][8];
-  auto load_step = [=](int t, u32x4 (&b)[8]) __attribute__((always_inline)) {
-    const int ch = t / nseg, seg = t - ch * nseg;
-    const uint32_t off = t < steps ? (uint32_t)((r0 + ch * 16 + l16) * K + seg * kResSegK + g * 8) * 2u : 0x80000000u;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      b[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off + ks * 64u, 0, 0));
-    // steps issue in order: a later step's load moved ahead of an earlier
-    // one makes the wait for the earlier one drain the queue
+    for (int s = 0; s < KS; ++s)
+      b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off + s * 64u, 0, 0));
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute_step = [&](int t, const u32x4 (&b)[8]) __attribute__((always_inline)) {
-    const int ch = t / nseg, seg = t - ch * nseg;
+  float bv[4];
+  int bi[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int c = seg * (kResSegK / 8) + ks * 4 + g;
-      const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
+  for (int e = 0; e < 4; ++e) {
+    bv[e] = -INFINITY;
+    bi[e] = -1;
+  }
+  auto chunk = [&](int j, const u32x4 (&b)[KS]) __attribute__((always_inline)) {
+    f32x4 acc[MQ];
 #pragma unroll
-      for (int i = 0; i < MQ; ++i) {
-        const int row = i * 16 + l16;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sa + row * K + res_swz(row, c) * 8);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[i], 0, 0, 0);
-      }
+    for (int i = 0; i < MQ; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, b[s]);
+#pragma unroll
+      for (int i = 0; i < MQ; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], bb, acc[i], 0, 0, 0);
     }
-    if (seg == nseg - 1) {                   // the chunk's logits are complete
-      const int col = ch * 16 + l16;         // row of the wave's run
-      const int gcol = r0 + col;
+    float (*rr)[16 * MQ][16] = red[j & 1];
 #pragma unroll
-      for (int i = 0; i < MQ; ++i)
+    for (int i = 0; i < MQ; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = bf2f(f2bf(acc[i][e]));
-          const bool take = col < nrows && cand_better(v, gcol, bv[i][e], bi[i][e]);
-          bv[i][e] = take ? v : bv[i][e];
-          bi[i][e] = take ? gcol : bi[i][e];
-          acc[i][e] = 0.f;
-        }
+      for (int e = 0; e < 4; ++e) rr[wave][i * 16 + 4 * g + e][l16] = acc[i][e];
+    __syncthreads();
+    if (wave < MQ) {
+      const int col = (c0 + j) * 16 + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = wave * 16 + 4 * g + e;
+        const float sum = ((rr[0][r][l16] + rr[1][r][l16]) + rr[2][r][l16]) + rr[3][r][l16];   // K order
+        const float v = bf2f(f2bf(sum));
+        const bool take = col < N && cand_better(v, col, bv[e], bi[e]);
+        bv[e] = take ? v : bv[e];
+        bi[e] = take ? col : bi[e];
+      }
     }
   };
-  // The loads are unconditional (past the run they load zeros without a
-  // memory access): with no branch around them the compiler's wait counts
-  // stay exact, where a conditional load makes later waits drain the queue.
 #pragma unroll
-  for (int p = 0; p < NB - 1; ++p) load_step(p, bfr[p]);
-  for (int t = 0; t < steps; t += NB) {
+  for (int p = 0; p < NB - 1; ++p) load_chunk(p, bfr[p]);
+  for (int j = 0; j < n; j += NB) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      load_step(t + u + NB - 1, bfr[(u + NB - 1) % NB]);
-      if (t + u < steps) compute_step(t + u, bfr[u]);
+      load_chunk(j + u + NB - 1, bfr[(u + NB - 1) % NB]);
+      if (j + u < n) chunk(j + u, bfr[u]);
     }
   }
-
-  // 3. lanes (the 16 of a row group), then waves, to one candidate per row
-#pragma unroll
-  for (int i = 0; i < MQ; ++i)
+  if (wave < MQ) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = bv[i][e];
-      int id = bi[i][e];
+      float v = bv[e];
+      int id = bi[e];
       cand_best16(v, id);
-      if (l16 == 0) {
-        s_v[wave][i * 16 + 4 * g + e] = v;
-        s_i[wave][i * 16 + 4 * g + e] = id;
-      }
+      const int r = wave * 16 + 4 * g + e;
+      if (l16 == 0 && r < M) cand[(int64_t)r * gridDim.x + blockIdx.x] = u32x2{__float_as_uint(v), (uint32_t)id};
     }
-  __syncthreads();
-  if (tid < RW && tid < M) {
-    float v = s_v[0][tid];
-    int id = s_i[0][tid];
-    for (int w = 1; w < NW; ++w)
-      if (cand_better(s_v[w][tid], s_i[w][tid], v, id)) {
-        v = s_v[w][tid];
-        id = s_i[w][tid];
-      }
-    cand[(int64_t)tid * gridDim.x + blockIdx.x] = u32x2{__float_as_uint(v), (uint32_t)id};
   }
 }
 
@@ -255,13 +216,22 @@ hipError_t argmax_resident(const void* x, int64_t M, const void* vocab, int64_t 
   const bf16* xb = static_cast<const bf16*>(x);
   const bf16* vb = static_cast<const bf16*>(vocab);
   u32x2* cb = static_cast<u32x2*>(cand);
-  // wave count and pipeline depth from a sweep on the 75968 x 1024 slice
-  if (M <= 16)
-    argmax_resident_kernel<4, 3, 1><<<kCUs, 256, 0, s>>>(xb, M, vb, N, (int)K, cb);
-  else if (M <= 32)
-    argmax_resident_kernel<8, 2, 2><<<kCUs, 512, 0, s>>>(xb, M, vb, N, (int)K, cb);
-  else
-    argmax_resident_kernel<8, 2, 4><<<kCUs, 512, 0, s>>>(xb, M, vb, N, (int)K, cb);
+  // chunks in flight per wave from a sweep on the 75968 x 1024 slice
+  auto go = [&](auto ks) {
+    constexpr int KS = decltype(ks)::value;
+    if (M <= 16)
+      argmax_resident_kernel<1, KS, 3><<<kCUs, 256, 0, s>>>(xb, M, vb, N, cb);
+    else if (M <= 32)
+      argmax_resident_kernel<2, KS, 3><<<kCUs, 256, 0, s>>>(xb, M, vb, N, cb);
+    else
+      argmax_resident_kernel<4, KS, 2><<<kCUs, 256, 0, s>>>(xb, M, vb, N, cb);
+  };
+  switch (K) {
+    case 256: go(std::integral_constant<int, 2>{}); break;
+    case 512: go(std::integral_constant<int, 4>{}); break;
+    case 768: go(std::integral_constant<int, 6>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
   return hipGetLastError();
 }
 

@@ -637,24 +637,25 @@ def test_lm_head_argmax_full_size_sampled(wid):
     check(gv, gi, rv, ri)
 
 
-@pytest.mark.parametrize("case", ["ragged-ties", "empty-shard", "rows-in-lds-ties", "rows-in-lds-empty-shard",
-                                  "rows-in-lds-one-row", "rows-in-lds-h256", "rows-in-lds-m20"])
+@pytest.mark.parametrize("case", ["ragged-ties", "empty-shard", "resident-ties", "resident-empty-shard",
+                                  "resident-one-row", "resident-h256", "resident-m20", "resident-h768"])
 def test_lm_head_argmax_ragged(case):
     """Odd local vocab sizes (row stride not a multiple of 16 bytes), uneven
     shards, planted exact ties across shards (the smallest id must win), and
-    an empty last shard that must never win.  The rows-in-LDS cases take the
-    resident-rows kernel (hidden a multiple of 256, up to 64 rows, in its
-    16-, 32- and 64-row forms): fewer vocab rows than waves (most waves get
-    none), one row, 20 rows, 64 rows."""
-    if case in ("ragged-ties", "rows-in-lds-ties"):
+    an empty last shard that must never win.  The resident cases take the
+    kernel that keeps the rows on chip (up to 64 rows, hidden 256, 512, 768
+    or 1024, in its 16-, 32- and 64-row forms): fewer vocab rows than
+    workgroups (most get none), one row, 20 rows, 50 rows, 64 rows."""
+    if case in ("ragged-ties", "resident-ties"):
         V, H, n, M = (1001, 520, 3, 37) if case == "ragged-ties" else (701, 256, 2, 37)
         out = _argmax_case(V, H, n, M, 13 if case == "ragged-ties" else 15, ties=True)
         assert (out[7][0::4] == 3).all()           # the oracle's winner is the first copy
     else:
-        V, H, n, M, wid = {"empty-shard": (5, 64, 4, 9, 14), "rows-in-lds-empty-shard": (5, 256, 4, 9, 18),
-                           "rows-in-lds-one-row": (151936, 1024, 2, 1, 16),
-                           "rows-in-lds-h256": (5003, 256, 3, 64, 17),
-                           "rows-in-lds-m20": (30011, 512, 2, 20, 19)}[case]
+        V, H, n, M, wid = {"empty-shard": (5, 64, 4, 9, 14), "resident-empty-shard": (5, 256, 4, 9, 18),
+                           "resident-one-row": (151936, 1024, 2, 1, 16),
+                           "resident-h256": (5003, 256, 3, 64, 17),
+                           "resident-m20": (30011, 512, 2, 20, 19),
+                           "resident-h768": (40009, 768, 2, 50, 20)}[case]
         out = _argmax_case(V, H, n, M, wid)
     gvr, gir, gv, gi, ov, oi, rv, ri, xc, Ec = out
     for r in range(n):
