@@ -112,7 +112,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const bf16* __restrict__ vocab, int64_t N,
                             u32x2* __restrict__ cand) {
   constexpr int K = KS * 128;                 // 4 waves x KS steps x 32
-  __shared__ float red[2][4][16 * MQ][16];
+  // rows padded to 20 floats: the four 16-lane groups of a wave write rows 4
+  // apart, which then start 16 banks apart instead of on the same banks
+  __shared__ float red[2][4][16 * MQ][20];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -159,7 +161,7 @@ void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const bf16* _
 #pragma unroll
       for (int i = 0; i < MQ; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], bb, acc[i], 0, 0, 0);
     }
-    float (*rr)[16 * MQ][16] = red[j & 1];
+    float (*rr)[16 * MQ][20] = red[j & 1];
 #pragma unroll
     for (int i = 0; i < MQ; ++i)
 #pragma unroll
