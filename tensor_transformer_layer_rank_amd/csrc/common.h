@@ -108,6 +108,12 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // RNE (v_cvt_pk_bf16_f32)
+// two floats to packed bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32, RNE
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 
 // --- GEMM -----------------------------------------------------------------
 // C[M, N] = A[M, K] * B[N, K]^T, A and B bf16 with K contiguous, fp32

@@ -492,6 +492,12 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   }
 }
 
+// 16-byte chunk swizzle of the persistent epilogue's 32 x 64 staging tile:
+// the 8-byte writes of one instruction cover 32 rows x one chunk, and rows
+// of equal parity start on the same bank, so the chunk is permuted by
+// (row / 2) % 8 to spread each parity's 16 rows over all 8 chunk slots.
+__device__ __forceinline__ int stage_swz(int r) { return (r >> 1) & 7; }
+
 // Persistent variant for grids of many tiles (bf16 and silu epilogues): one
 // workgroup per CU walks a share of the tiles of its XCD, and the LDS ring
 // runs on across tile boundaries, so the next tile's first block is already
@@ -499,7 +505,10 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 // workgroup launch, pipeline fill or ring drain separates two tiles.  The
 // epilogue stages each wave's outputs, 32 rows x 64 columns at a time,
 // through a 4 KB LDS region of its own next to the ring, so it needs no
-// workgroup barrier and never touches a ring stage.
+// workgroup barrier and never touches a ring stage.  The MFMAs take the B
+// (weight) fragment as their first operand and so accumulate C^T: each lane
+// then holds four consecutive output columns of one row, staged by one
+// 8-byte LDS write instead of four 2-byte ones.
 //
 // Tile order: the tiles (GROUP_M-grouped as in gemm_kernel) are cut into 8
 // contiguous ranges, one per XCD; workgroup b runs on XCD b % 8 (the
@@ -655,7 +664,7 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   auto mfma_pair = [&](int fs, int pr) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m)
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
+      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fs][m % TN], af[fs][m / TN],
                                                                   acc[m / TN][m % TN], 0, 0, 0);
   };
   // the block just landed in `buf` is read next: all waves have their
@@ -687,23 +696,28 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = 8 * (e >> 2) + 4 * lh + (e & 3), c = jj * 32 + lr;
-            float v;
-            if (EPI == EPI_SILU_BF16) {
-              const float g = acc[i][ps * 2 + jj][e], u = acc[i][ps * 2 + jj + TN / 2][e];
-              v = g / (1.f + __expf(-g)) * u;
-            } else {
-              v = acc[i][ps * 2 + jj][e];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int e = 4 * g4 + q;
+              if (EPI == EPI_SILU_BF16) {
+                const float g = acc[i][ps * 2 + jj][e], u = acc[i][ps * 2 + jj + TN / 2][e];
+                v[q] = g / (1.f + __expf(-g)) * u;
+              } else {
+                v[q] = acc[i][ps * 2 + jj][e];
+              }
             }
-            so[r * 64 + (((c >> 3) ^ (r & 7)) << 3) + (c & 7)] = f2bf(v);
+            // row lr, columns jj * 32 + 8 * g4 + 4 * lh .. + 3: one 8-byte write
+            const u32x2 w{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(so + lr * 64 + (((jj * 4 + g4) ^ stage_swz(lr)) << 3) + 4 * lh) = w;
           }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int q = lane + 64 * u, r = q >> 3, cc = q & 7;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * 64 + ((cc ^ (r & 7)) << 3));
+          const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * 64 + ((cc ^ stage_swz(r)) << 3));
           const int64_t gm = m0 + wm * WM + i * 32 + r, gc = col0 + ps * 64 + cc * 8;
           if (gm < M && gc < ncols) {
             if (vec && gc + 8 <= ncols) {
