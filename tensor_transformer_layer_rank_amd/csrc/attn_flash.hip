@@ -28,6 +28,8 @@
 // MFMAs of S for tile i + 1 are in flight while the VALU runs the softmax
 // of tile i.  Decode, bound by the stream of K and V, keeps K and V of one
 // tile per stage (one more tile of loads in flight).
+#include <type_traits>
+
 #include "common.h"
 #include "qkv_finish.h"
 
@@ -227,7 +229,8 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   };
   // online softmax of tile kt's scores s, then O^T += V^T P^T with the V
   // tile in stage st
-  auto soft_pv = [&](f32x16 s, int kt, int st) {
+  // (s is the caller's tile, masked in place: it is dead afterwards)
+  auto soft_pv = [&](f32x16& s, int kt, int st) {
     const unsigned char* V = ring + st * kStageB + kTileB;
     const int key0 = kt * kKeys;
     // V^T operands do not depend on P: their transposing reads go out first
@@ -274,14 +277,14 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
     }
     const float base = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 pf[2];
-    float ps = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};    // four short chains instead of one of 16
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float pv = ex2(__builtin_fmaf(s[e], kQScale, -base));   // masked: 2^-inf = 0
-      ps += pv;
+      ps[e & 3] += pv;
       pf[e >> 3][e & 7] = f2bf(pv);
     }
-    l_run += ps;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -302,7 +305,8 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
       } else {
         wait_vm<0>();
       }
-      soft_pv(s_tile(i % NST), w0 + i, i % NST);
+      f32x16 sc = s_tile(i % NST);
+      soft_pv(sc, w0 + i, i % NST);
     }
   } else if (n > 0) {
     // stage j = {K of tile w0 + j, V of tile w0 + j - 1}, j = 0 .. n, in
@@ -313,23 +317,29 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
     dma_tile(w0, 0);
     dma_tile(w0 + 1, 1);
     wait_vm<SL>();
-    f32x16 s_cur = s_tile(0);
+    f32x16 s_a = s_tile(0), s_b = s_a;
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage 0 read
     if (2 <= n) dma_tile(w0 + 2, 0);
-    for (int i = 0; i < n; ++i) {
-      const int st = (i + 1) & 1;
+    // iteration i: S of tile i is in `cur`, S of tile i + 1 goes to `nxt`;
+    // unrolled by two so that the stage (i + 1) % 2 is a constant (LDS
+    // offsets fold into the instructions) and S alternates between s_a and
+    // s_b without copies
+    auto step = [&](int i, auto st_tag, f32x16& cur, f32x16& nxt) __attribute__((always_inline)) {
+      constexpr int st = decltype(st_tag)::value;
       if (i + 2 <= n)
         wait_vm<SL>();
       else
         wait_vm<0>();
-      f32x16 s_next = s_cur;
-      if (i + 1 < n) s_next = s_tile(st);
-      soft_pv(s_cur, w0 + i, st);
-      s_cur = s_next;
+      nxt = s_tile(st);   // on the last tile: a settled stage, result unused
+      soft_pv(cur, w0 + i, st);
       if (i + 3 <= n) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage i + 1 read
         dma_tile(w0 + i + 3, st);
       }
+    };
+    for (int i = 0; i < n; i += 2) {
+      step(i, std::integral_constant<int, 1>{}, s_a, s_b);
+      if (i + 1 < n) step(i + 1, std::integral_constant<int, 0>{}, s_b, s_a);
     }
   }
 
