@@ -107,6 +107,10 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 block");
   static_assert(EPI != EPI_SILU_BF16 || (TN % 2 == 0), "silu pairs need an even number of n-blocks");
+  // bf16 outputs accumulate C^T (B fragment as the first MFMA operand): a
+  // lane then holds four consecutive output columns of one row, staged by
+  // one 8-byte LDS write
+  constexpr bool TR = EPI == EPI_BF16 || EPI == EPI_SILU_BF16;
   constexpr int STAGE = (BM + BN) * BK;
   // LDS ring of S stages: S - 1 blocks in flight
   static_assert(S >= 2 && S * STAGE * 2 <= 163840, "ring must be double-buffered and fit the CU's LDS");
@@ -238,9 +242,14 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   };
   auto mfma_pair = [&](int fs, int pr) {
 #pragma unroll
-    for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m)
-      acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
-                                                                  acc[m / TN][m % TN], 0, 0, 0);
+    for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m) {
+      if constexpr (TR)
+        acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fs][m % TN], af[fs][m / TN],
+                                                                    acc[m / TN][m % TN], 0, 0, 0);
+      else
+        acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
+                                                                    acc[m / TN][m % TN], 0, 0, 0);
+    }
   };
   const bool tail = (kend - kbeg) % BK != 0;
   auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
@@ -339,7 +348,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   if (kt < nk) block(std::false_type{}, std::false_type{}, kt);                     // last block
 
   // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
-  // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block.
+  // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block (transposed for TR).
   if constexpr (EPI == EPI_ARGMAX) {
     // Greedy-decode candidates: per tile row, the largest bf16-rounded
     // value over the tile's columns and the first column holding it (ties
@@ -447,25 +456,27 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   // reading for the last K block
   __syncthreads();
   auto so_idx = [&](int r, int c) { return r * OC + (((c >> 3) ^ (r & (OCH - 1))) << 3) + (c & 7); };
-  if (EPI == EPI_SILU_BF16) {
+  // (C^T layout: row i * 32 + lr, columns j * 32 + 8 * g4 + 4 * lh .. + 3)
 #pragma unroll
-    for (int j = 0; j < TN / 2; ++j)
+  for (int j = 0; j < (EPI == EPI_SILU_BF16 ? TN / 2 : TN); ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
-          so[so_idx(i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), j * 32 + lr)] = f2bf(g / (1.f + __expf(-g)) * u);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * g4 + q;
+          if (EPI == EPI_SILU_BF16) {
+            const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
+            v[q] = g / (1.f + __expf(-g)) * u;
+          } else {
+            v[q] = acc[i][j][e];
+          }
         }
-  } else {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          so[so_idx(i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), j * 32 + lr)] = f2bf(acc[i][j][e]);
-  }
+        *reinterpret_cast<u32x2*>(so + so_idx(i * 32 + lr, j * 32 + 8 * g4 + 4 * lh)) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
   __builtin_amdgcn_wave_barrier();
   const int64_t ncols = EPI == EPI_SILU_BF16 ? p.li : p.N;
