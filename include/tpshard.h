@@ -27,13 +27,17 @@
  * Conventions for every entry point
  *   - All tensors are caller-owned, contiguous, row-major device memory
  *     (allocated with hipMalloc or by PyTorch).  The library allocates
- *     nothing and keeps no global state; calls are re-entrant.
+ *     nothing; its only state is the per-thread timing marks of
+ *     tp_kernel_marks (off unless armed); calls are re-entrant.
  *   - Weights use the [out, in] layout of a linear layer (the input dimension
  *     is contiguous).  Element type is cfg->dtype: TP_BF16 (bfloat16 bits)
  *     or TP_F32.
  *   - Every pointer argument must be 16-byte aligned (TP_ERR_ALIGN).
  *   - Arguments are validated on the host before anything is launched; on a
- *     non-zero return nothing has been written.  Work is enqueued on
+ *     non-zero return nothing has been written.  Row lengths of GEMM operands
+ *     (hidden, the local intermediate, lq * head_dim) must be below 2^22
+ *     elements and S_max below 2^24 (TP_ERR_SHAPE): the kernels address a
+ *     tile or a cache slab through 32-bit buffer descriptors.  Work is enqueued on
  *     `stream` (a hipStream_t; NULL = the null stream) and runs
  *     asynchronously; TP_ERR_LAUNCH reports a failed launch.
  *   - Collectives are not part of the library: a row-parallel call returns
@@ -127,6 +131,29 @@ int tp_workspace_bytes(const tp_cfg* cfg, int op, int64_t B, int64_t T, int64_t 
 
 /* Static description of a status code. */
 const char* tp_status_str(int status);
+
+/* ------------------------------------------------------------------------
+ * Per-kernel timing marks (instrumentation; host thread-local state)
+ * ---------------------------------------------------------------------- */
+
+/* tp_kernel_marks -- arms the calling host thread: the device entry points it
+ * calls next record events[i] on the call's stream right after launching
+ * their i-th kernel (counting across calls), for i < n_events; later kernels
+ * are not marked.  events are hipEvent_t handles created by the caller (with
+ * timing enabled) and must stay valid while armed; the array itself is
+ * copied.  The time from an event the caller records before the first call
+ * to mark 0, and from mark i-1 to mark i, is the stream time of each kernel
+ * (launch gaps included).  events = NULL with n_events = 0 disarms.  Errors:
+ * n_events < 0 -> TP_ERR_RANGE; events NULL with n_events > 0 -> TP_ERR_NULL. */
+int tp_kernel_marks(void* const* events, int32_t n_events);
+
+/* Marks recorded since the last tp_kernel_marks call on this thread. */
+int32_t tp_kernel_marks_used(void);
+
+/* Name of the kernel launched just before mark i on this thread, e.g.
+ * "gemm_tile<256,256,2>/silu" or "attn_flash/decode"; "" when i is out of
+ * range.  Valid until the next tp_kernel_marks call on this thread. */
+const char* tp_kernel_mark_name(int32_t i);
 
 /* ------------------------------------------------------------------------
  * Device entry points

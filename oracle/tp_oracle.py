@@ -175,9 +175,9 @@ def embed_vocab(ids, table_local, vocab_start, vocab_end):
     return out
 
 
-def lm_head(x, table_local, store=bf16):
+def lm_head(x, table_local, store=bf16, ft=np.float64):
     """Local slice of the logits: x @ table_local^T."""
-    return store(np.asarray(x, np.float64) @ np.asarray(table_local, np.float64).T)
+    return store(np.asarray(x, ft) @ np.asarray(table_local, ft).T)
 
 
 # Greedy decode over vocab-parallel logits ([TPS] Implementation: the next
@@ -227,10 +227,10 @@ def argmax_combine(vals, idx):
 # attention block pieces   ([TPS] Implementation, TPAttention.forward)
 # --------------------------------------------------------------------------
 
-def rms_norm(v, w, eps):
+def rms_norm(v, w, eps, ft=np.float64):
     """Normalise the last axis to unit RMS, then scale by w."""
-    v = np.asarray(v, np.float64)
-    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * np.asarray(w, np.float64)
+    v = np.asarray(v, ft)
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * np.asarray(w, ft)
 
 
 def rope_angles(positions, head_dim, theta):
@@ -240,45 +240,45 @@ def rope_angles(positions, head_dim, theta):
     return np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]
 
 
-def rope(v, positions, theta):
+def rope(v, positions, theta, ft=np.float64):
     """Rotate-half RoPE on the last axis; v is [rows, heads, d] and
     positions is [rows]."""
-    v = np.asarray(v, np.float64)
+    v = np.asarray(v, ft)
     d = v.shape[-1]
     ang = rope_angles(positions, d, theta)[:, None, :]
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = np.cos(ang).astype(ft), np.sin(ang).astype(ft)
     x1, x2 = v[..., : d // 2], v[..., d // 2:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def q_heads(c: Cfg, x, w_qkv_local, q_norm_w, positions, store=bf16):
+def q_heads(c: Cfg, x, w_qkv_local, q_norm_w, positions, store=bf16, ft=np.float64):
     """q part of the merged column-parallel projection: the rank's lq heads,
     QK-norm per head, then RoPE at each row's position; [rows, lq, d]."""
     L = local_dims(c)
     d = c.head_dim
-    w = np.asarray(w_qkv_local, np.float64)[: L.lq * d]
-    q = (np.asarray(x, np.float64) @ w.T).reshape(-1, L.lq, d)
-    return store(rope(rms_norm(q, q_norm_w, c.rms_eps), positions, c.rope_theta))
+    w = np.asarray(w_qkv_local, ft)[: L.lq * d]
+    q = (np.asarray(x, ft) @ w.T).reshape(-1, L.lq, d)
+    return store(rope(rms_norm(q, q_norm_w, c.rms_eps, ft), positions, c.rope_theta, ft))
 
 
-def kv_heads(c: Cfg, x, w_qkv_local, k_norm_w, positions, store=bf16):
+def kv_heads(c: Cfg, x, w_qkv_local, k_norm_w, positions, store=bf16, ft=np.float64):
     """k and v parts of the merged projection: k gets QK-norm and RoPE, v
     neither; each [rows, lkv, d]."""
     L = local_dims(c)
     d = c.head_dim
-    w = np.asarray(w_qkv_local, np.float64)
-    x = np.asarray(x, np.float64)
+    w = np.asarray(w_qkv_local, ft)
+    x = np.asarray(x, ft)
     k = (x @ w[L.lq * d:(L.lq + L.lkv) * d].T).reshape(-1, L.lkv, d)
     v = (x @ w[(L.lq + L.lkv) * d:].T).reshape(-1, L.lkv, d)
-    k = rope(rms_norm(k, k_norm_w, c.rms_eps), positions, c.rope_theta)
+    k = rope(rms_norm(k, k_norm_w, c.rms_eps, ft), positions, c.rope_theta, ft)
     return store(k), store(v)
 
 
-def qkv_heads(c: Cfg, x, w_qkv_local, q_norm_w, k_norm_w, positions, store=bf16):
+def qkv_heads(c: Cfg, x, w_qkv_local, q_norm_w, k_norm_w, positions, store=bf16, ft=np.float64):
     """Merged column-parallel projection split into the rank's heads:
     stored (q, k, v) as [rows, heads, d]."""
-    k, v = kv_heads(c, x, w_qkv_local, k_norm_w, positions, store)
-    return q_heads(c, x, w_qkv_local, q_norm_w, positions, store), k, v
+    k, v = kv_heads(c, x, w_qkv_local, k_norm_w, positions, store, ft)
+    return q_heads(c, x, w_qkv_local, q_norm_w, positions, store, ft), k, v
 
 
 def attend(q_rows, q_pos, k_seq, v_seq, rep):
@@ -289,7 +289,7 @@ def attend(q_rows, q_pos, k_seq, v_seq, rep):
     kv head i // rep; query at position p sees keys 0..p.  Returns float64
     [n, lq, d] (unrounded)."""
     n, lq, d = q_rows.shape
-    out = np.zeros((n, lq, d))
+    out = np.zeros((n, lq, d), q_rows.dtype)
     scale = 1.0 / math.sqrt(d)
     for a in range(n):
         p = int(q_pos[a])
@@ -303,27 +303,29 @@ def attend(q_rows, q_pos, k_seq, v_seq, rep):
 
 
 def qkv_attn(c: Cfg, x, B, T, past, w_qkv_local, q_norm_w, k_norm_w, w_o_local,
-             k_cache, v_cache, store=bf16):
+             k_cache, v_cache, store=bf16, ft=np.float64):
     """One call of the attention shard: B sequences with T new tokens each at
     positions past..past+T-1.  Writes k/v into copies of the caches
     [B, lkv, S_max, d] and returns dict(q, k_cache, v_cache, attn, partial),
-    q/attn as [B*T, lq*d] and the row-parallel partial [B*T, H]."""
+    q/attn as [B*T, lq*d] and the row-parallel partial [B*T, H].
+    ft: the arithmetic type (float64 for parity; float32 only to time the
+    CPU baseline, whose store must then return float32 too)."""
     L = local_dims(c)
     d = c.head_dim
     rep = L.lq // L.lkv
-    x = np.asarray(x, np.float64)
+    x = np.asarray(x, ft)
     pos = np.tile(np.arange(past, past + T), B)
-    q, k, v = qkv_heads(c, x, w_qkv_local, q_norm_w, k_norm_w, pos, store)
-    kc = np.array(k_cache, dtype=np.float64, copy=True)
-    vc = np.array(v_cache, dtype=np.float64, copy=True)
-    attn = np.zeros((B * T, L.lq, d))
+    q, k, v = qkv_heads(c, x, w_qkv_local, q_norm_w, k_norm_w, pos, store, ft)
+    kc = np.array(k_cache, dtype=ft, copy=True)
+    vc = np.array(v_cache, dtype=ft, copy=True)
+    attn = np.zeros((B * T, L.lq, d), ft)
     for b in range(B):
         rows = slice(b * T, (b + 1) * T)
         kc[b, :, past:past + T] = k[rows].transpose(1, 0, 2)
         vc[b, :, past:past + T] = v[rows].transpose(1, 0, 2)
         attn[rows] = attend(q[rows], pos[rows], kc[b, :, : past + T], vc[b, :, : past + T], rep)
     attn = store(attn.reshape(B * T, L.lq * d))
-    partial = store(attn @ np.asarray(w_o_local, np.float64).T)
+    partial = store(attn @ np.asarray(w_o_local, ft).T)
     return dict(q=q.reshape(B * T, L.lq * d), k_cache=kc, v_cache=vc, attn=attn, partial=partial)
 
 
@@ -400,16 +402,16 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def mlp(c: Cfg, x, w_gate_up_local, w_down_local, store=bf16):
+def mlp(c: Cfg, x, w_gate_up_local, w_down_local, store=bf16, ft=np.float64):
     """h = silu(x Wg^T) * (x Wu^T) on the local intermediate slice, then the
     row-parallel partial h Wd^T.  Returns (h, partial), both stored."""
     li = local_dims(c).li
-    x = np.asarray(x, np.float64)
-    w = np.asarray(w_gate_up_local, np.float64)
+    x = np.asarray(x, ft)
+    w = np.asarray(w_gate_up_local, ft)
     g = x @ w[:li].T
     u = x @ w[li:].T
     h = store(silu(g) * u)
-    return h, store(h @ np.asarray(w_down_local, np.float64).T)
+    return h, store(h @ np.asarray(w_down_local, ft).T)
 
 
 # --------------------------------------------------------------------------

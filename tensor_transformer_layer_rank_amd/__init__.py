@@ -20,9 +20,9 @@ TP_F32, TP_BF16 = 0, 1
 TP_W_Q, TP_W_K, TP_W_V, TP_W_O, TP_W_GATE, TP_W_UP, TP_W_DOWN, TP_W_VOCAB = range(8)
 TP_OP_ATTN, TP_OP_MLP, TP_OP_LM_ARGMAX = 0, 1, 2
 
-EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_shard_weights", "tp_embed_vocab",
-           "tp_qkv_attn", "tp_mlp", "tp_lm_head", "tp_lm_head_argmax", "tp_argmax_combine",
-           "tp_residual_rmsnorm", "tp_sp_rows", "tp_sp_residual_rmsnorm")
+EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_kernel_marks", "tp_kernel_marks_used",
+           "tp_kernel_mark_name", "tp_shard_weights", "tp_embed_vocab", "tp_qkv_attn", "tp_mlp", "tp_lm_head",
+           "tp_lm_head_argmax", "tp_argmax_combine", "tp_residual_rmsnorm", "tp_sp_rows", "tp_sp_residual_rmsnorm")
 
 
 class TpError(RuntimeError):
@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.tp_workspace_bytes.argtypes = [C, ctypes.c_int, I64, I64, I64, ctypes.POINTER(SZ)]
         L.tp_status_str.argtypes = [ctypes.c_int]
         L.tp_status_str.restype = ctypes.c_char_p
+        L.tp_kernel_marks.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
+        L.tp_kernel_marks_used.argtypes = []
+        L.tp_kernel_mark_name.argtypes = [I32]
+        L.tp_kernel_mark_name.restype = ctypes.c_char_p
         L.tp_shard_weights.argtypes = [C, ctypes.c_int, P, P, P]
         L.tp_embed_vocab.argtypes = [C, P, I64, P, P, P]
         L.tp_qkv_attn.argtypes = [C, P, I32, I32, I32, P, P, P, P, P, P, I32, P, P, P, P, SZ, P]
@@ -97,7 +101,7 @@ def lib() -> ctypes.CDLL:
         L.tp_sp_rows.argtypes = [C, I64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.tp_sp_residual_rmsnorm.argtypes = [C, P, I64, P, P, P, P, P]
         for name in EXPORTS:
-            if name != "tp_status_str":
+            if name not in ("tp_status_str", "tp_kernel_mark_name"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -145,6 +149,30 @@ def tp_workspace_bytes(cfg: Cfg, op: int, B: int, T: int, past_len: int = 0) -> 
 
 def tp_status_str(status: int) -> str:
     return lib().tp_status_str(status).decode()
+
+
+def tp_kernel_marks(events):
+    """Arms per-kernel timing marks on this thread: `events` are
+    torch.cuda.Event(enable_timing=True) objects, recorded in order after each
+    kernel that the following calls launch.  An empty list disarms."""
+    import torch
+    handles = []
+    for e in events:
+        if e.cuda_event == 0:          # torch creates the event at its first record
+            e.record(torch.cuda.current_stream())
+        handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * max(len(handles), 1))(*handles)
+    _check(lib().tp_kernel_marks(arr if handles else None, len(handles)))
+
+
+def tp_kernel_marks_used() -> int:
+    return lib().tp_kernel_marks_used()
+
+
+def tp_kernel_mark_names() -> list:
+    """Names of the kernels marked since the last tp_kernel_marks call."""
+    L = lib()
+    return [L.tp_kernel_mark_name(i).decode() for i in range(L.tp_kernel_marks_used())]
 
 
 def tp_shard_weights(cfg: Cfg, kind: int, full, dst, stream=None):

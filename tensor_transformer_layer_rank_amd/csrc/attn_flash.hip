@@ -405,6 +405,7 @@ hipError_t attn_flash(const AttnArgs& a, hipStream_t s) {
     attn_flash_kernel<4, 2, false><<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
   else
     attn_flash_kernel<4, 2, true><<<(unsigned)blocks, 256, 0, s>>>(a, n_rb);
+  kmark(s, a.T == 1 ? "attn_flash/decode" : "attn_flash/prefill");
   return hipGetLastError();
 }
 

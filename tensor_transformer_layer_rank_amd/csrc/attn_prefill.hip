@@ -378,6 +378,7 @@ template <int HW, int HG>
 hipError_t launch(const AttnArgs& a, const PrefillPlan& p, hipStream_t s) {
   const int64_t groups = (int64_t)a.B * a.lkv * p.hgroups;
   attn_prefill_kernel<HW, HG, kStages><<<(unsigned)(groups * p.n_rb), 256, 0, s>>>(a, p);
+  kmark(s, "attn_prefill");
   return hipGetLastError();
 }
 

@@ -233,4 +233,11 @@ hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t plane, int64_t 
 // threads that residual_rmsnorm gives one row of M x H (64 .. 1024)
 int norm_threads_per_row(int64_t M, int H);
 
+// --- per-kernel timing marks (tp_kernel_marks, host thread-local) ---------
+// After each kernel launch the launching code calls kmark: when the calling
+// host thread has armed marks, the next event is recorded on `s` and the
+// kernel's name kept beside it; otherwise nothing happens.
+bool kmarks_armed();
+void kmark(hipStream_t s, const char* name);
+
 }  // namespace tps

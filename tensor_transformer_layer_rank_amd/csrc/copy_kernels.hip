@@ -84,6 +84,7 @@ hipError_t copy2d(const void* src, int64_t src_ld, int64_t row0, int64_t col0, v
     copy2d_scalar<uint16_t><<<grid_for(rows * cols), kThreads, 0, s>>>(
         reinterpret_cast<const uint16_t*>(sp), src_ld, reinterpret_cast<uint16_t*>(dp), dst_ld, rows, cols);
   }
+  kmark(s, v16 ? "copy2d_v16" : "copy2d_scalar");
   return hipGetLastError();
 }
 
@@ -93,6 +94,7 @@ hipError_t embed_masked(const int32_t* ids, int64_t n, const void* table, int64_
   const int64_t row_b = H * esize;   // the caller guarantees row_b % 16 == 0
   embed_masked_v16<<<grid_for(n * (row_b / 16)), kThreads, 0, s>>>(
       ids, n, static_cast<const uint8_t*>(table), vstart, vend, row_b, static_cast<uint8_t*>(out));
+  kmark(s, "embed_masked_v16");
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include <algorithm>
+#include <cstdio>
 
 #include "common.h"
 #include "qkv_finish.h"
@@ -1012,6 +1013,15 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
   return best;
 }
 
+// timing mark after a GEMM-family launch: kernel, tile and epilogue
+const char* const kEpiNames[] = {"bf16", "f32", "silu", "qkv", "argmax"};
+void mark_gemm(hipStream_t s, const char* kern, int bm, int bn, int stages, int epi) {
+  if (!kmarks_armed()) return;
+  char buf[96];
+  snprintf(buf, sizeof buf, "%s<%d,%d,%d>/%s", kern, bm, bn, stages, kEpiNames[epi]);
+  kmark(s, buf);
+}
+
 // finish = false: a split plan stops after the partials (the consumer sums
 // them itself)
 template <int BM, int BN, int WGM, int WGN, int S>
@@ -1025,6 +1035,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     q.ldc = p.N;
     dim3 grid(pl.tiles_m * pl.tiles_n, pl.splits);
     gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
+    mark_gemm(s, "gemm_splitk", BM, BN, S, epi);
     if (!finish) return hipGetLastError();
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
     int64_t g = (p.M * (cols / 4) + 255) / 256;
@@ -1039,18 +1050,21 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
       splitk_reduce<EPI_BF16><<<(int)g, 256, 0, s>>>((const float*)scratch, pl.splits, p.M, p.N, p.C, p.ldc, 0);
     else
       splitk_reduce<EPI_F32><<<(int)g, 256, 0, s>>>((const float*)scratch, pl.splits, p.M, p.N, p.C, p.ldc, 0);
+    kmark(s, epi == EPI_QKV ? "splitk_reduce/qkv" : "splitk_reduce");
     return hipGetLastError();
   }
   dim3 grid(pl.tiles_m * pl.tiles_n);
   if constexpr ((BN / WGN / 32) % 2 == 0) {
     if (epi == EPI_SILU_BF16) {
       gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_SILU_BF16);
       return hipGetLastError();
     }
   }
   if constexpr (qkv_tile_ok(BM, BN, S)) {
     if (epi == EPI_QKV) {
       gemm_kernel<BM, BN, WGM, WGN, EPI_QKV, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_QKV);
       return hipGetLastError();
     }
   }
@@ -1058,12 +1072,14 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
     gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+    mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX);
     return hipGetLastError();
   }
   if (epi == EPI_BF16)
     gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   else
     gemm_kernel<BM, BN, WGM, WGN, EPI_F32, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+  mark_gemm(s, "gemm_tile", BM, BN, S, epi);
   return hipGetLastError();
 }
 
@@ -1120,6 +1136,7 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
   // fill and relaunch it saves are a visible part of a tile's time)
   if (pl.v == V256x256 && pl.splits == 1 && epi == EPI_BF16 && (int64_t)pl.tiles_m * pl.tiles_n >= 8 * kCUs) {
     gemm_persist_kernel<256, 256, 4, 2, EPI_BF16, 8, 2><<<kCUs, 512, 0, s>>>(p, pl.tiles_m, pl.tiles_n);
+    mark_gemm(s, "gemm_persist", 256, 256, 2, EPI_BF16);
     return hipGetLastError();
   }
   switch (pl.v) {
@@ -1164,6 +1181,7 @@ hipError_t gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t
   int64_t g = (M * cols + 255) / 256;
   if (g > 8192) g = 8192;
   gemm_f32_kernel<<<(int)g, 256, 0, s>>>(A, B, C, M, N, K, silu_li);
+  kmark(s, silu_li > 0 ? "gemm_f32/silu" : "gemm_f32");
   return hipGetLastError();
 }
 

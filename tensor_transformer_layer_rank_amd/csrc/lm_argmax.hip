@@ -234,6 +234,7 @@ hipError_t argmax_resident(const void* x, int64_t M, const void* vocab, int64_t 
     case 768: go(std::integral_constant<int, 6>{}); break;
     default: go(std::integral_constant<int, 8>{}); break;
   }
+  kmark(s, "argmax_resident");
   return hipGetLastError();
 }
 
@@ -241,6 +242,7 @@ hipError_t argmax_candidates(const void* cand, int64_t M, int64_t n, int64_t idx
                              hipStream_t s) {
   if (M <= 0) return hipSuccess;
   argmax_pairs<<<(unsigned)M, 256, 0, s>>>(static_cast<const u32x2*>(cand), n, idx0, out_val, out_idx);
+  kmark(s, "argmax_pairs");
   return hipGetLastError();
 }
 
@@ -250,6 +252,7 @@ hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, i
   int64_t g = (M + 255) / 256;
   if (g > 1024) g = 1024;
   combine_candidates<<<(unsigned)g, 256, 0, s>>>(vals, idx, n_shards, M, out_idx, out_val);
+  kmark(s, "combine_candidates");
   return hipGetLastError();
 }
 

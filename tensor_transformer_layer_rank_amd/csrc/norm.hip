@@ -156,6 +156,7 @@ hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t plane, int64_t 
     case 512: launch_norm_tpr<512>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
     default: launch_norm_tpr<1024>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
   }
+  kmark(s, "residual_rmsnorm");
   return hipGetLastError();
 }
 

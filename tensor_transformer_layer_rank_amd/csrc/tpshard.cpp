@@ -9,11 +9,32 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <string>
+#include <vector>
 
 #include "../../include/tpshard.h"
 #include "common.h"
 
 using namespace tps;
+
+// Per-kernel timing marks (tp_kernel_marks): per host thread, the caller's
+// events and the names of the kernels marked so far.
+namespace {
+struct KernelMarks {
+  std::vector<hipEvent_t> events;
+  std::vector<std::string> names;
+};
+thread_local KernelMarks g_marks;
+}  // namespace
+
+namespace tps {
+bool kmarks_armed() { return g_marks.names.size() < g_marks.events.size(); }
+void kmark(hipStream_t s, const char* name) {
+  if (!kmarks_armed()) return;
+  (void)hipEventRecord(g_marks.events[g_marks.names.size()], s);
+  g_marks.names.emplace_back(name);
+}
+}  // namespace tps
 
 namespace {
 
@@ -113,6 +134,16 @@ LmWs lm_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
 
 int launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
 
+// The kernels read through buffer descriptors whose byte range is 32-bit.
+// A GEMM tile's descriptor starts at the tile's first row and its loads
+// reach at most 256 rows of the operand, so a row length (K, in elements)
+// below 2^22 keeps every offset under 2^31; an attention descriptor covers
+// one (sequence, kv head) slab of 256-byte cache rows, so positions stay
+// below 2^24.
+constexpr int64_t kMaxRowElems = int64_t(1) << 22;
+constexpr int64_t kMaxPositions = int64_t(1) << 24;
+bool row_ok(int64_t k) { return k > 0 && k < kMaxRowElems; }
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +151,21 @@ extern "C" {
 int tp_local_dims(const tp_cfg* cfg, tp_local* out) {
   if (!out) return TP_ERR_NULL;
   return check_cfg(cfg, out);
+}
+
+int tp_kernel_marks(void* const* events, int32_t n_events) {
+  if (n_events < 0) return TP_ERR_RANGE;
+  if (n_events > 0 && !events) return TP_ERR_NULL;
+  g_marks.events.assign(reinterpret_cast<const hipEvent_t*>(events),
+                        reinterpret_cast<const hipEvent_t*>(events) + n_events);
+  g_marks.names.clear();
+  return TP_OK;
+}
+
+int32_t tp_kernel_marks_used(void) { return (int32_t)g_marks.names.size(); }
+
+const char* tp_kernel_mark_name(int32_t i) {
+  return i >= 0 && (size_t)i < g_marks.names.size() ? g_marks.names[i].c_str() : "";
 }
 
 const char* tp_status_str(int s) {
@@ -230,6 +276,7 @@ int tp_qkv_attn(const tp_cfg* cfg, const void* x, int32_t B, int32_t T, int32_t 
   if (st) return st;
   if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
   if (L.lq == 0 || cfg->head_dim != 128 || cfg->hidden % 8) return TP_ERR_SHAPE;
+  if (!row_ok(cfg->hidden) || !row_ok((int64_t)L.lq * 128) || S_max >= kMaxPositions) return TP_ERR_SHAPE;
   const int rep = L.lq / L.lkv;
   if (L.lq % L.lkv || (rep != 1 && rep != 2 && rep != 4 && rep != 8 && rep != 16)) return TP_ERR_SHAPE;
   if (B < 0 || T < 0 || past_len < 0 || S_max < 0) return TP_ERR_RANGE;
@@ -289,6 +336,7 @@ int tp_mlp(const tp_cfg* cfg, const void* x, int64_t M, const void* w_gate_up, c
   int st = check_cfg(cfg, &L);
   if (st) return st;
   if (L.li == 0 || cfg->hidden % 8 || L.li % 8) return TP_ERR_SHAPE;
+  if (!row_ok(cfg->hidden) || !row_ok(L.li)) return TP_ERR_SHAPE;
   if (M < 0) return TP_ERR_RANGE;
   if (!x || !w_gate_up || !w_down || !out_partial) return TP_ERR_NULL;
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out_partial) ||
@@ -327,7 +375,7 @@ int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_lo
   tp_local L;
   int st = check_cfg(cfg, &L);
   if (st) return st;
-  if (cfg->vocab == 0 || cfg->hidden % 8) return TP_ERR_SHAPE;
+  if (cfg->vocab == 0 || cfg->hidden % 8 || !row_ok(cfg->hidden)) return TP_ERR_SHAPE;
   if (M < 0) return TP_ERR_RANGE;
   if (!x || !vocab_local || !logits_local) return TP_ERR_NULL;
   if (!aligned16(x) || !aligned16(vocab_local) || !aligned16(logits_local)) return TP_ERR_ALIGN;
@@ -347,7 +395,7 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* v
   int st = check_cfg(cfg, &L);
   if (st) return st;
   if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
-  if (cfg->vocab == 0 || cfg->hidden % 8) return TP_ERR_SHAPE;
+  if (cfg->vocab == 0 || cfg->hidden % 8 || !row_ok(cfg->hidden)) return TP_ERR_SHAPE;
   if (M < 0) return TP_ERR_RANGE;
   if (!x || !vocab_local || !out_val || !out_idx) return TP_ERR_NULL;
   if (!aligned16(x) || !aligned16(vocab_local) || ((uintptr_t)out_val & 3) || ((uintptr_t)out_idx & 3))

@@ -1,7 +1,10 @@
 """Host-side tests of the C ABI: the library loads, exports every symbol the
 header declares, and validates arguments before any launch.  No GPU work:
 every device entry point here is called with arguments that validation
-rejects (or with an empty size), so nothing is enqueued."""
+rejects (or with an empty size), so nothing is enqueued.  Those calls pass
+fake device addresses, so they run only where no GPU is visible: on a GPU
+host a regression in the validation order would launch a kernel on an
+unmapped address instead of failing an assertion."""
 import ctypes
 import os
 import re
@@ -20,7 +23,7 @@ OK, E_NULL, E_RANK, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_RANGE, E_LAUNCH, E_KIND =
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(tp_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|const char\*|size_t)\s+(tp_\w+)\s*\(", src, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -87,6 +90,18 @@ def test_config_errors():
     assert tp.tp_status_str(E_WS) == "workspace too small"
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+# device entry points called with fake addresses: host-only
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses are only passed where no GPU is visible")
+
+
 class Fake:
     """A stand-in 'tensor' with a fake device address; used only where the
     library must reject the call before launching anything."""
@@ -112,6 +127,7 @@ A = Fake(1 << 40)           # 16-byte aligned
 MIS = Fake((1 << 40) + 8)   # misaligned
 
 
+@host_only
 def test_shard_and_embed_validation():
     c = tp.Cfg(hidden=64, intermediate=192, n_q_heads=4, n_kv_heads=2, vocab=100, tp_size=2)
     s = NullStream()
@@ -127,6 +143,7 @@ def test_shard_and_embed_validation():
     assert _status(tp.tp_embed_vocab, c, Fake(1 << 40, 5), None, A, s) == E_NULL
 
 
+@host_only
 def test_attn_validation():
     c = tp.Cfg(hidden=256, intermediate=512, n_q_heads=4, n_kv_heads=2, head_dim=128, tp_size=2)
     s = NullStream()
@@ -156,6 +173,7 @@ def test_attn_validation():
     assert need >= 2 * (2 * 3) * 2 * 128 * 2           # at least the q and attention-output buffers
 
 
+@host_only
 def test_mlp_and_lm_head_validation():
     c = tp.Cfg(hidden=256, intermediate=512, tp_size=2)
     s = NullStream()
@@ -172,6 +190,7 @@ def test_mlp_and_lm_head_validation():
     assert _status(tp.tp_lm_head, tp.Cfg(hidden=256, tp_size=1), A, 4, A, A, s) == E_SHAPE
 
 
+@host_only
 def test_lm_head_argmax_and_combine_validation():
     s = NullStream()
     cv = tp.Cfg(hidden=256, vocab=1000, tp_size=4, tp_rank=3)
@@ -208,6 +227,7 @@ def test_lm_head_argmax_workspace_paths():
         assert need != M * 256 * 8                                  # the logits-GEMM path
 
 
+@host_only
 def test_residual_rmsnorm_validation():
     s = NullStream()
     c = tp.Cfg(hidden=256, tp_size=2)
@@ -229,6 +249,7 @@ def test_sp_rows_match_oracle(M, n):
         assert tp.tp_sp_rows(tp.Cfg(hidden=64, tp_size=n, tp_rank=r), M) == O.sp_rows(M, n, r)
 
 
+@host_only
 def test_sp_residual_rmsnorm_validation():
     s = NullStream()
     c = tp.Cfg(hidden=256, tp_size=4, tp_rank=3)
@@ -242,3 +263,36 @@ def test_sp_residual_rmsnorm_validation():
     assert _status(tp.tp_sp_residual_rmsnorm, tp.Cfg(hidden=260, tp_size=4), A, 8, A, A, A, A, s) == E_SHAPE
     assert _status(tp.tp_sp_residual_rmsnorm, tp.Cfg(hidden=256, tp_size=4, dtype=tp.TP_F32),
                    A, 8, A, A, A, A, s) == E_DTYPE
+
+
+def test_kernel_marks_host_logic():
+    """Arming and disarming the per-kernel timing marks is host-only state:
+    no event is recorded until a device entry point launches a kernel."""
+    L = tp.lib()
+    assert L.tp_kernel_marks(None, 0) == OK
+    assert L.tp_kernel_marks(None, -1) == E_RANGE
+    assert L.tp_kernel_marks(None, 3) == E_NULL
+    assert L.tp_kernel_marks_used() == 0
+    assert L.tp_kernel_mark_name(0) == b""
+    assert L.tp_kernel_mark_name(-1) == b""
+
+
+@host_only
+def test_descriptor_range_limits():
+    """Buffer-descriptor byte ranges are 32-bit: the kernels address a tile's
+    rows (at most 256 of them) and a cache slab's positions relative to one
+    base, so a row length of 2^22 elements or more, or an S_max of 2^24 or
+    more, is rejected on the host."""
+    s = NullStream()
+    big = 1 << 22
+    c = tp.Cfg(hidden=256, intermediate=512, n_q_heads=4, n_kv_heads=2, head_dim=128, tp_size=2)
+    ws = Fake(1 << 40, 1 << 30, 1)
+    assert _status(tp.tp_qkv_attn, c, A, 1, 1, 0, A, A, A, A, A, A, 1 << 24, A, ws, None, None, s) == E_SHAPE
+    cb = tp.Cfg(hidden=big, intermediate=512, n_q_heads=4, n_kv_heads=2, head_dim=128, tp_size=2)
+    assert _status(tp.tp_qkv_attn, cb, A, 1, 1, 0, A, A, A, A, A, A, 8, A, ws, None, None, s) == E_SHAPE
+    assert _status(tp.tp_mlp, tp.Cfg(hidden=big, intermediate=512, tp_size=2), A, 4, A, A, A, ws, None, s) == E_SHAPE
+    assert _status(tp.tp_mlp, tp.Cfg(hidden=256, intermediate=2 * big, tp_size=2), A, 4, A, A, A, ws, None,
+                   s) == E_SHAPE
+    cv = tp.Cfg(hidden=big, vocab=1000, tp_size=2)
+    assert _status(tp.tp_lm_head, cv, A, 4, A, A, s) == E_SHAPE
+    assert _status(tp.tp_lm_head_argmax, cv, A, 4, A, A, A, ws, s) == E_SHAPE

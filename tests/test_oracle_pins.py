@@ -571,3 +571,37 @@ def test_sp_residual_rmsnorm_gathers_to_torch(M, n):
     np.testing.assert_array_equal(O.all_gather(ys), yt.double().numpy())
     h_full, y_full = O.residual_rmsnorm(P, res, w, eps)
     np.testing.assert_array_equal(O.all_gather(ys), y_full)
+
+
+def test_float32_variant_tracks_float64():
+    """The float32 variant (used only to time the CPU baseline) computes the
+    same maths: without storage rounding it stays within float32 rounding of
+    the float64 oracle, and with bf16 stores within one bf16 step."""
+    c = O.Cfg(**{**TINY.__dict__, "tp_size": 2, "tp_rank": 1})
+    W = _tiny_full()
+    L = O.local_dims(c)
+    B, T, past = 2, 3, 4
+    x = O.bf16(_rand(40, (B * T, c.hidden)))
+    pk = O.bf16(_rand(41, (B, c.n_kv_heads, past, c.head_dim)))
+    pv = O.bf16(_rand(42, (B, c.n_kv_heads, past, c.head_dim)))
+    qkv, wo, gu, wd = _rank_weights(c, W)
+    S_max = past + T + 2
+    kc = np.zeros((B, L.lkv, S_max, c.head_dim))
+    vc = np.zeros_like(kc)
+    kc[:, :, :past] = pk[:, L.kv_head0:L.kv_head0 + L.lkv]
+    vc[:, :, :past] = pv[:, L.kv_head0:L.kv_head0 + L.lkv]
+    f32 = np.float32
+    for store64, store32, tol in ((_ident, lambda v: np.asarray(v, f32), 1e-5),
+                                  (O.bf16, lambda v: O.bf16(v).astype(f32), 2 ** -7)):
+        r64 = O.qkv_attn(c, x, B, T, past, qkv, W["qn"], W["kn"], wo, kc, vc, store=store64)
+        r32 = O.qkv_attn(c, x.astype(f32), B, T, past, qkv.astype(f32), W["qn"].astype(f32),
+                         W["kn"].astype(f32), wo.astype(f32), kc.astype(f32), vc.astype(f32),
+                         store=store32, ft=f32)
+        assert r32["partial"].dtype == f32
+        for k in ("q", "attn", "partial"):
+            rel = np.max(np.abs(r32[k] - r64[k])) / np.max(np.abs(r64[k]))
+            assert rel <= tol, (k, rel)
+        h64, p64 = O.mlp(c, x, gu, wd, store=store64)
+        h32, p32 = O.mlp(c, x.astype(f32), gu.astype(f32), wd.astype(f32), store=store32, ft=f32)
+        assert p32.dtype == f32
+        assert np.max(np.abs(p32 - p64)) / np.max(np.abs(p64)) <= tol
