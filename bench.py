@@ -3,6 +3,7 @@
 layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-extra]
+                    [--only kv_stream|vocab]
 
 The timed step (default workload qwen3-32b-tp2: Qwen3-32B at tp=2, rank 0)
 runs every row of the hot path once, in this order:
@@ -350,6 +351,10 @@ def run_bench(args):
              (tp.TP_W_GATE, "gate", "gu"), (tp.TP_W_UP, "up", "gu"), (tp.TP_W_DOWN, "down", "down"))
     torch.cuda.set_device(0)
 
+    if args.only == "kv_stream":
+        return extra_kv_stream(tp, synth, args, {}), None
+    if args.only == "vocab":
+        return extra_vocab(tp, synth, args, {}), None
     # ---- the timed step: every row of the path on the main workload -------------
     P = Problem(tp, synth, args.workload, set(FULL_PHASES))
     sets = P.sets()
@@ -428,48 +433,63 @@ def run_bench(args):
     }
 
     # ---- beside the step: the KV stream (32B tp=16 decode) and the 0.6B lm_head -
-    if not args.no_extra and args.workload == "qwen3-32b-tp2":
-        PK = Problem(tp, synth, "qwen3-32b-tp16", {"decode"})
-        ks = PK.sets()
-        torch.cuda.synchronize()
-        _, kph, kk = time_steps(tp, PK, ks, ["decode"], args.steps, args.warmup)
-        del ks
-        kdb = bytes_decode(PK.w, PK.L, PK.B, PK.ctx)
-        ka_name, ka_t = find_kernel(kk, "decode", lambda s: s.startswith("attn_flash/decode"))
-        ka_bytes = kdb["kv"] + 2 * PK.B * PK.L.lq * 128 * 2
-        ka_gbps = ka_bytes / ka_t / 1e9
-        w_t = sum(t for p, nm, t in kk if not nm.startswith("attn_flash"))
-        out["kv_stream"] = {
-            "workload": f"qwen3-32b-tp16 rank 0 decode: B={PK.B} at KV context {PK.ctx}, 1 replicated kv head "
-                        f"(4 local q heads)",
-            "decode_GBps": round(sum(kdb.values()) / kph["decode"] / 1e9, 1),
-            "decode_us": round(kph["decode"] * 1e6, 2),
-            "attention_GBps": round(ka_gbps, 1), "attention_us": round(ka_t * 1e6, 2),
-            "attention_pct_hbm_peak": round(100 * ka_gbps / HBM_PEAK_GBPS, 2),
-            "weight_stream_us": round(w_t * 1e6, 2),
-            "weight_stream_GBps": round(kdb["weights"] / w_t / 1e9, 1),
-            "kernel_us": kernel_table(kk)}
-        out["roofline_hbm"] = {
-            "kernel": f"{ka_name} (tp_qkv_attn decode attention, KV stream B={PK.B} x ctx {PK.ctx})",
-            "bound": "hbm", "achieved": round(ka_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(ka_gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(ka_t * 1e6, 2),
-            "algorithmic_bytes_per_launch": ka_bytes,
-            "traffic": traffic_from_profile("decode_attention_qwen3-32b-tp16_hbm_traffic.txt", "attn_flash.hip")}
-        del PK
-        PL = Problem(tp, synth, "qwen3-0.6b-tp2", {"embed", "lm_head"})
-        ls = PL.sets()
-        torch.cuda.synchronize()
-        _, lph, lk = time_steps(tp, PL, ls, ["embed", "lm_head"], args.steps, args.warmup)
-        del ls
-        l_flops = 2 * PL.n_ids * PL.nv * PL.H
-        out["vocab_0.6b"] = {
-            "workload": f"qwen3-0.6b-tp2 rank 0: embed + lm_head over {PL.n_ids} ids, hidden {PL.H}, "
-                        f"local vocab {PL.nv}",
-            "lm_head_TFLOPs": round(l_flops / lph["lm_head"] / 1e12, 1),
-            "lm_head_pct_mfma_peak": round(100 * l_flops / lph["lm_head"] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
-            "embed_us": round(lph["embed"] * 1e6, 2), "kernel_us": kernel_table(lk)}
-        del PL
+    if not args.no_extra and args.workload == "qwen3-32b-tp2" and args.only is None:
+        extra_kv_stream(tp, synth, args, out)
+        extra_vocab(tp, synth, args, out)
     return out, P
+
+
+def extra_kv_stream(tp, synth, args, out):
+    """The decode layer of Qwen3-32B at tp=16 (rank 0): B=256 at KV context
+    4096 over one replicated kv head; the attention kernel is the KV stream."""
+    import torch
+    PK = Problem(tp, synth, "qwen3-32b-tp16", {"decode"})
+    ks = PK.sets()
+    torch.cuda.synchronize()
+    _, kph, kk = time_steps(tp, PK, ks, ["decode"], args.steps, args.warmup)
+    del ks
+    kdb = bytes_decode(PK.w, PK.L, PK.B, PK.ctx)
+    ka_name, ka_t = find_kernel(kk, "decode", lambda s: s.startswith("attn_flash/decode"))
+    ka_bytes = kdb["kv"] + 2 * PK.B * PK.L.lq * 128 * 2
+    ka_gbps = ka_bytes / ka_t / 1e9
+    w_t = sum(t for p, nm, t in kk if not nm.startswith("attn_flash"))
+    out["kv_stream"] = {
+        "workload": f"qwen3-32b-tp16 rank 0 decode: B={PK.B} at KV context {PK.ctx}, 1 replicated kv head "
+                    f"(4 local q heads)",
+        "decode_GBps": round(sum(kdb.values()) / kph["decode"] / 1e9, 1),
+        "decode_us": round(kph["decode"] * 1e6, 2),
+        "attention_GBps": round(ka_gbps, 1), "attention_us": round(ka_t * 1e6, 2),
+        "attention_pct_hbm_peak": round(100 * ka_gbps / HBM_PEAK_GBPS, 2),
+        "weight_stream_us": round(w_t * 1e6, 2),
+        "weight_stream_GBps": round(kdb["weights"] / w_t / 1e9, 1),
+        "kernel_us": kernel_table(kk)}
+    out["roofline_hbm"] = {
+        "kernel": f"{ka_name} (tp_qkv_attn decode attention, KV stream B={PK.B} x ctx {PK.ctx})",
+        "bound": "hbm", "achieved": round(ka_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(ka_gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(ka_t * 1e6, 2),
+        "algorithmic_bytes_per_launch": ka_bytes,
+        "traffic": traffic_from_profile("decode_attention_qwen3-32b-tp16_hbm_traffic.txt", "attn_flash.hip")}
+    del PK
+    return out
+
+
+def extra_vocab(tp, synth, args, out):
+    """The vocab-parallel embedding + lm_head of Qwen3-0.6B at tp=2 (rank 0)."""
+    import torch
+    PL = Problem(tp, synth, "qwen3-0.6b-tp2", {"embed", "lm_head"})
+    ls = PL.sets()
+    torch.cuda.synchronize()
+    _, lph, lk = time_steps(tp, PL, ls, ["embed", "lm_head"], args.steps, args.warmup)
+    del ls
+    l_flops = 2 * PL.n_ids * PL.nv * PL.H
+    out["vocab_0.6b"] = {
+        "workload": f"qwen3-0.6b-tp2 rank 0: embed + lm_head over {PL.n_ids} ids, hidden {PL.H}, "
+                    f"local vocab {PL.nv}",
+        "lm_head_TFLOPs": round(l_flops / lph["lm_head"] / 1e12, 1),
+        "lm_head_pct_mfma_peak": round(100 * l_flops / lph["lm_head"] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+        "embed_us": round(lph["embed"] * 1e6, 2), "kernel_us": kernel_table(lk)}
+    del PL
+    return out
 
 
 def cpu_baseline(w, seconds_hint=20.0):
@@ -532,13 +552,16 @@ def main():
     ap.add_argument("--workload", default="qwen3-32b-tp2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the KV-stream and 0.6B lm_head measurements")
+    ap.add_argument("--only", choices=["kv_stream", "vocab"], default=None,
+                    help="run only one of the measurements beside the step (for profiling); prints its object")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the shard of one tensor-parallel rank runs on a single MI355X; "
               "collectives across GPUs are not part of this library.  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     out, P = run_bench(args)
-    out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(P.w)
+    if P is not None:
+        out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(P.w)
     print(json.dumps(out), flush=True)
 
 
