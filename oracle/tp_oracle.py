@@ -203,6 +203,40 @@ def lm_head_argmax(x, table_local, vocab_start, store=bf16):
     return vals, idx
 
 
+# Last-token selection and the final norm before the head ([TPS]
+# Implementation, TPTransformer.forward: the final RMSNorm runs on x[:, -1:],
+# each sequence's last position; [CH9] 3.3, ParallelLMHead: in prefill only
+# each sequence's last row reaches the vocab-split linear).  With sequences
+# of different lengths packed one after another, sequence b's last row is
+# the sum of the lengths up to and including b, minus one.
+
+def last_token_rows(seq_lens):
+    """Row of each sequence's last token in the packed [sum(lens), H] batch."""
+    rows, end = [], 0
+    for n in seq_lens:
+        if n < 1:
+            raise ValueError("a sequence has no token")
+        end += int(n)
+        rows.append(end - 1)
+    return np.asarray(rows, np.int64)
+
+
+def gather_rows(x, rows):
+    """x[rows]; an index outside [0, len(x)) gives a zero row (the library
+    reads such a row through a bounds-checked load as zeros)."""
+    x = np.asarray(x)
+    out = np.zeros((len(rows),) + x.shape[1:], x.dtype)
+    for m, r in enumerate(rows):
+        if 0 <= r < x.shape[0]:
+            out[m] = x[r]
+    return out
+
+
+def rmsnorm_rows(x, rows, w, eps, store=bf16):
+    """The final norm on the selected rows: store(rms_norm(x[rows]) * w)."""
+    return store(rms_norm(gather_rows(x, rows), w, eps))
+
+
 def argmax_combine(vals, idx):
     """vals, idx: [n_shards, M] candidates.  Per row the largest value; among
     equal values the smallest global index; shards with no vocabulary carry

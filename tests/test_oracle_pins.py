@@ -605,3 +605,63 @@ def test_float32_variant_tracks_float64():
         h32, p32 = O.mlp(c, x.astype(f32), gu.astype(f32), wd.astype(f32), store=store32, ft=f32)
         assert p32.dtype == f32
         assert np.max(np.abs(p32 - p64)) / np.max(np.abs(p64)) <= tol
+
+
+# ---- last-token selection and the final norm before the head ----------------
+
+def test_last_token_rows_match_torch_indexing():
+    """Equal lengths: the rows x.view(B, T, H)[:, -1] picks ([TPS]
+    TPTransformer.forward, x[:, -1:]); ragged lengths: the last row of each
+    piece that torch.split cuts the packed batch into."""
+    B, T = 4, 5
+    idx = torch.arange(B * T).view(B, T)[:, -1]
+    assert np.array_equal(O.last_token_rows([T] * B), idx.numpy())
+    lens = [3, 1, 7, 2]
+    pieces = torch.split(torch.arange(sum(lens)), lens)
+    assert np.array_equal(O.last_token_rows(lens), np.array([p[-1].item() for p in pieces]))
+    with pytest.raises(ValueError):
+        O.last_token_rows([2, 0])
+
+
+def test_rmsnorm_rows_commutes_with_selection():
+    """Norm after selection ([TPS] order) equals selection after norm over
+    all rows ([CH9] order), and equals torch's rms_norm on the selected rows;
+    an index outside the batch gives a zero row."""
+    rng = np.random.default_rng(50)
+    x = O.bf16(rng.standard_normal((9, 48)))
+    w = O.bf16(rng.uniform(0.5, 1.5, 48))
+    rows = np.array([8, 2, 2, 5])
+    y = O.rmsnorm_rows(x, rows, w, 1e-6, store=_ident)
+    y_all = O.rms_norm(x, w, 1e-6)
+    assert np.allclose(y, y_all[rows], rtol=0, atol=1e-12)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x)[torch.from_numpy(rows)], (48,),
+                                       torch.from_numpy(w), eps=1e-6).numpy()
+    assert np.allclose(y, ref, rtol=0, atol=1e-12)
+    z = O.rmsnorm_rows(x, np.array([0, 9, -1]), w, 1e-6, store=_ident)
+    assert np.array_equal(z[1:], np.zeros((2, 48))) and np.allclose(z[0], y_all[0])
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_decode_head_on_last_tokens_equals_torch(n):
+    """Greedy next token of each sequence from the last rows, normed, over n
+    vocab shards equals torch.argmax of F.linear(rms_norm(x[:, -1:]), E)."""
+    rng = np.random.default_rng(51 + n)
+    B, T, H, V = 3, 4, 32, 50
+    x = O.bf16(rng.standard_normal((B * T, H)))
+    w = O.bf16(rng.uniform(0.5, 1.5, H))
+    E = O.bf16(rng.standard_normal((V, H)) * 0.3)
+    rows = O.last_token_rows([T] * B)
+    y = O.rmsnorm_rows(x, rows, w, 1e-6)
+    vals, idx = [], []
+    for r in range(n):
+        c = O.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=r)
+        L = O.local_dims(c)
+        v, i = O.lm_head_argmax(y, O.shard(c, O.W_VOCAB, E), L.vocab_start)
+        vals.append(v)
+        idx.append(i)
+    _, tok = O.argmax_combine(np.stack(vals), np.stack(idx))
+    xt = torch.from_numpy(x).view(B, T, H)[:, -1:]
+    yt = torch.nn.functional.rms_norm(xt, (H,), torch.from_numpy(w), eps=1e-6)
+    yt = torch.from_numpy(O.bf16(yt.numpy()))
+    logits = torch.from_numpy(O.bf16(torch.nn.functional.linear(yt, torch.from_numpy(E)).numpy()))
+    assert np.array_equal(tok, torch.argmax(logits[:, -1], dim=-1).numpy())
