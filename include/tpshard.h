@@ -229,12 +229,18 @@ int tp_mlp(const tp_cfg* cfg, const void* x, int64_t M, const void* w_gate_up,
 /* tp_lm_head -- the rank's slice of the logits before the all-gather ([CH9]
  * 3.3 ParallelLMHead; [TPS] "Implementation", the vocab-split output layer,
  * tied to the embedding shard when the model ties them):
- *   logits_local = x @ vocab_local^T
- * x: [M, H]; vocab_local: [vocab_end - vocab_start, H];
- * logits_local: [M, vocab_end - vocab_start].  Which rows to run (e.g. only
- * each sequence's last token) is the caller's choice.  M = 0: no-op. */
-int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local,
-               void* logits_local, void* stream);
+ *   logits_local[m] = x[row m] @ vocab_local^T,   m < M
+ * Rows: with rows_opt NULL, row m of x (x: [M, H], x_rows ignored); with
+ * rows_opt an int32 device array [M] of indices into x [x_rows, H], row
+ * rows_opt[m] -- the head's last-token selection ([CH9] 3.3: in prefill
+ * only each sequence's last row reaches the head; tp_last_token_rows gives
+ * those indices).  An index outside [0, x_rows) reads as a zero row (its
+ * logits are 0).  A row list needs TP_BF16 (TP_ERR_DTYPE), x_rows >= 1
+ * (TP_ERR_RANGE), 4-byte alignment (TP_ERR_ALIGN) and x_rows * H * 2 < 2^31
+ * (TP_ERR_SHAPE).  vocab_local: [vocab_end - vocab_start, H];
+ * logits_local: [M, vocab_end - vocab_start].  M = 0: no-op. */
+int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const int32_t* rows_opt, int64_t x_rows,
+               const void* vocab_local, void* logits_local, void* stream);
 
 /* tp_lm_head_argmax -- this rank's greedy candidate per row ([TPS]
  * "Implementation": decode takes the argmax of the last position's logits;
@@ -245,15 +251,17 @@ int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_lo
  *   out_idx[m] = vocab_start + first n attaining it (a global token id)
  * An empty vocab slice gives (-inf, -1).  The candidates of all ranks
  * (gathered into [n_shards, M]) combine with tp_argmax_combine.
- * x: bf16 [M, H]; vocab_local: bf16 [vocab_end - vocab_start, H];
+ * x, rows_opt, x_rows: the rows of the head, as for tp_lm_head (x bf16).
+ * vocab_local: bf16 [vocab_end - vocab_start, H];
  * out_val: float [M]; out_idx: int32 [M];
  * workspace >= tp_workspace_bytes(cfg, TP_OP_LM_ARGMAX, M, 1, 0), 16-byte
  * aligned: it holds 8-byte partial candidates (per row and logits tile, or per
  * row and workgroup when up to 64 rows with H <= 1024, H % 256 == 0 keep x
  * resident on chip); the logits themselves are never stored.  Requires
  * TP_BF16 (TP_ERR_DTYPE) and H % 8 == 0.  M = 0: no-op. */
-int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local,
-                      float* out_val, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const int32_t* rows_opt, int64_t x_rows,
+                      const void* vocab_local, float* out_val, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                      void* stream);
 
 /* tp_argmax_combine -- the cross-shard step of the greedy argmax: per row the
  * candidate with the largest value, ties to the smallest token id (the first
@@ -275,10 +283,35 @@ int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, i
  * out_partial, stacked: on one GPU this stands in for the all-reduce);
  * residual, h_out, y_out: bf16 [M, H]; norm_w: bf16 [H].  h_out may be the
  * residual buffer (in-place update of the residual stream); y_out must not
- * overlap the inputs.  Requires TP_BF16 (TP_ERR_DTYPE), H % 8 == 0 and
- * H <= 8192 (TP_ERR_SHAPE), n_partials >= 1 (TP_ERR_RANGE).  M = 0: no-op. */
+ * overlap the inputs.  n_partials = 0 is the plain RMSNorm of the residual
+ * (the final norm before the head; partials and h_out may then be NULL).
+ * Requires TP_BF16 (TP_ERR_DTYPE), H % 8 == 0 and H <= 8192 (TP_ERR_SHAPE),
+ * n_partials >= 0 (TP_ERR_RANGE).  M = 0: no-op. */
 int tp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int32_t n_partials, int64_t M,
                         const void* residual, const void* norm_w, void* h_out, void* y_out, void* stream);
+
+/* tp_rmsnorm_rows -- the final RMSNorm on selected rows before the head
+ * ([TPS] "Implementation", TPTransformer.forward: norm(x[:, -1:]), each
+ * sequence's last position):
+ *   y[m] = bf16(x[i] / sqrt(mean(x[i]^2) + rms_eps) * norm_w),  m < n_rows,
+ *   i = rows[m] (rows: int32 device array [n_rows]) or i = m (rows NULL,
+ *   n_rows <= x_rows)
+ * x: bf16 [x_rows, H]; norm_w: bf16 [H]; y_out: bf16 [n_rows, H].  An index
+ * outside [0, x_rows) gives a zero row; a row list needs x_rows >= 1
+ * (TP_ERR_RANGE).  Requires TP_BF16 (TP_ERR_DTYPE),
+ * H % 8 == 0 and H <= 8192 (TP_ERR_SHAPE); rows 4-byte aligned.
+ * n_rows = 0: no-op. */
+int tp_rmsnorm_rows(const tp_cfg* cfg, const void* x, int64_t x_rows, const int32_t* rows, int64_t n_rows,
+                    const void* norm_w, void* y_out, void* stream);
+
+/* tp_last_token_rows -- host only, no HIP call: the row of each sequence's
+ * last token in a batch of n_seqs sequences packed one after another
+ * ([CH9] 3.3: the head keeps each sequence's last index; [TPS]
+ * "Implementation": x[:, -1:]):  rows_out[b] = seq_lens[0] + ... +
+ * seq_lens[b] - 1.  seq_lens, rows_out: host int32 arrays [n_seqs].  A
+ * length < 1 or n_seqs < 0 -> TP_ERR_RANGE; a sum past 2^31 - 1 ->
+ * TP_ERR_SHAPE. */
+int tp_last_token_rows(const int32_t* seq_lens, int32_t n_seqs, int32_t* rows_out);
 
 /* tp_sp_rows -- host only, no HIP call: rank tp_rank's token slice
  * [*row0, *row1) of M tokens under sequence parallelism ([TPS] "Exercises",

@@ -22,7 +22,8 @@ TP_OP_ATTN, TP_OP_MLP, TP_OP_LM_ARGMAX = 0, 1, 2
 
 EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_kernel_marks", "tp_kernel_marks_used",
            "tp_kernel_mark_name", "tp_shard_weights", "tp_embed_vocab", "tp_qkv_attn", "tp_mlp", "tp_lm_head",
-           "tp_lm_head_argmax", "tp_argmax_combine", "tp_residual_rmsnorm", "tp_sp_rows", "tp_sp_residual_rmsnorm")
+           "tp_lm_head_argmax", "tp_argmax_combine", "tp_residual_rmsnorm", "tp_rmsnorm_rows", "tp_last_token_rows",
+           "tp_sp_rows", "tp_sp_residual_rmsnorm")
 
 
 class TpError(RuntimeError):
@@ -94,10 +95,12 @@ def lib() -> ctypes.CDLL:
         L.tp_embed_vocab.argtypes = [C, P, I64, P, P, P]
         L.tp_qkv_attn.argtypes = [C, P, I32, I32, I32, P, P, P, P, P, P, I32, P, P, P, P, SZ, P]
         L.tp_mlp.argtypes = [C, P, I64, P, P, P, P, P, SZ, P]
-        L.tp_lm_head.argtypes = [C, P, I64, P, P, P]
-        L.tp_lm_head_argmax.argtypes = [C, P, I64, P, P, P, P, SZ, P]
+        L.tp_lm_head.argtypes = [C, P, I64, P, I64, P, P, P]
+        L.tp_lm_head_argmax.argtypes = [C, P, I64, P, I64, P, P, P, P, SZ, P]
         L.tp_argmax_combine.argtypes = [P, P, I32, I64, P, P, P]
         L.tp_residual_rmsnorm.argtypes = [C, P, I32, I64, P, P, P, P, P]
+        L.tp_rmsnorm_rows.argtypes = [C, P, I64, P, I64, P, P, P]
+        L.tp_last_token_rows.argtypes = [ctypes.POINTER(I32), I32, ctypes.POINTER(I32)]
         L.tp_sp_rows.argtypes = [C, I64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.tp_sp_residual_rmsnorm.argtypes = [C, P, I64, P, P, P, P, P]
         for name in EXPORTS:
@@ -198,15 +201,20 @@ def tp_mlp(cfg: Cfg, x, M: int, w_gate_up, w_down, out_partial, workspace, h_out
                         _ptr(out_partial), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def tp_lm_head(cfg: Cfg, x, M: int, vocab_local, logits_local, stream=None):
-    _check(lib().tp_lm_head(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(vocab_local), _ptr(logits_local),
-                            _stream(stream)))
+def _x_rows(x, rows):
+    return 0 if rows is None else x.shape[0]
 
 
-def tp_lm_head_argmax(cfg: Cfg, x, M: int, vocab_local, out_val, out_idx, workspace, stream=None):
+def tp_lm_head(cfg: Cfg, x, M: int, vocab_local, logits_local, stream=None, rows=None):
+    """rows: optional int32 device tensor [M] of row indices into x."""
+    _check(lib().tp_lm_head(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(rows), _x_rows(x, rows), _ptr(vocab_local),
+                            _ptr(logits_local), _stream(stream)))
+
+
+def tp_lm_head_argmax(cfg: Cfg, x, M: int, vocab_local, out_val, out_idx, workspace, stream=None, rows=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().tp_lm_head_argmax(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(vocab_local), _ptr(out_val), _ptr(out_idx),
-                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    _check(lib().tp_lm_head_argmax(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(rows), _x_rows(x, rows), _ptr(vocab_local),
+                                   _ptr(out_val), _ptr(out_idx), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def tp_argmax_combine(vals, idx, n_shards: int, M: int, out_idx, out_val=None, stream=None):
@@ -216,6 +224,21 @@ def tp_argmax_combine(vals, idx, n_shards: int, M: int, out_idx, out_val=None, s
 def tp_residual_rmsnorm(cfg: Cfg, partials, n_partials: int, M: int, residual, norm_w, h_out, y_out, stream=None):
     _check(lib().tp_residual_rmsnorm(ctypes.byref(cfg.c()), _ptr(partials), n_partials, M, _ptr(residual),
                                      _ptr(norm_w), _ptr(h_out), _ptr(y_out), _stream(stream)))
+
+
+def tp_rmsnorm_rows(cfg: Cfg, x, rows, n_rows: int, norm_w, y_out, stream=None):
+    """y_out[m] = RMSNorm(x[rows[m]]) * norm_w; rows None: x rows 0..n_rows-1."""
+    _check(lib().tp_rmsnorm_rows(ctypes.byref(cfg.c()), _ptr(x), 0 if x is None else x.shape[0], _ptr(rows), n_rows,
+                                 _ptr(norm_w), _ptr(y_out), _stream(stream)))
+
+
+def tp_last_token_rows(seq_lens):
+    """Row of each sequence's last token in the packed batch (a list)."""
+    n = len(seq_lens)
+    lens = (ctypes.c_int32 * max(n, 1))(*seq_lens)
+    out = (ctypes.c_int32 * max(n, 1))()
+    _check(lib().tp_last_token_rows(lens, n, out))
+    return list(out)[:n]
 
 
 def tp_sp_rows(cfg: Cfg, M: int):

@@ -150,6 +150,11 @@ struct GemmProblem {
   int64_t lda, ldb, ldc;
   int64_t li;           // EPI_SILU_BF16 only
   QkvArgs qkv;          // EPI_QKV only
+  // optional row gather of A: row m of the product reads A row a_rows[m]
+  // (an index outside [0, a_total) reads as a zero row); a_total * lda * 2
+  // must be below 2^31.  Never used with EPI_QKV or a split plan.
+  const int32_t* a_rows;
+  int64_t a_total;
 };
 
 // Chooses a tile shape and launches.  When the grid would not fill the GPU
@@ -218,18 +223,36 @@ hipError_t argmax_candidates(const void* cand, int64_t M, int64_t n, int64_t idx
 // the vocab slice.
 bool argmax_resident_ok(int64_t M, int64_t N, int64_t K);
 int argmax_resident_groups();
-hipError_t argmax_resident(const void* x, int64_t M, const void* vocab, int64_t N, int64_t K, void* cand,
-                           hipStream_t s);
+// rows: optional row list (row m reads x row rows[m]; outside [0, x_rows):
+// zeros), with x_rows * K * 2 < 2^31
+hipError_t argmax_resident(const void* x, int64_t M, const int32_t* rows, int64_t x_rows, const void* vocab,
+                           int64_t N, int64_t K, void* cand, hipStream_t s);
 // out_idx[m] = the candidate (vals, idx [n_shards, M]) with the largest
 // value, ties to the smallest index, idx < 0 skipped; out_val optional.
 hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, int64_t M, int32_t* out_idx,
                           float* out_val, hipStream_t s);
 
 // --- residual + RMSNorm over summed row-parallel partials -----------------
-// h = bf16(residual + sum_r partials[r * plane]), y = bf16(rms_norm(h) * w)
-// over M rows of H; H % 8 == 0 and H <= 8192; h_out may alias residual.
-hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
-                            const bf16* w, float eps, bf16* h_out, bf16* y_out, hipStream_t s);
+// For output row m < M, with input row i = in_rows ? in_rows[m] : m (an i
+// outside [0, in_nrows) reads as a zero row):
+//   h[m] = bf16(residual[i] + sum_{r < n} partials[r * plane + i])
+//   y[m] = bf16(rms_norm(h[m]) * w)
+// H % 8 == 0 and H <= 8192; h_out may alias residual, and may be NULL when
+// n == 0 (plain RMSNorm).
+struct NormArgs {
+  const bf16* partials;
+  int n;
+  int64_t plane, M;
+  int H;
+  const bf16* residual;
+  const bf16* w;
+  float eps;
+  bf16* h_out;
+  bf16* y_out;
+  const int32_t* in_rows;
+  int64_t in_nrows;
+};
+hipError_t residual_rmsnorm(const NormArgs& a, hipStream_t s);
 // threads that residual_rmsnorm gives one row of M x H (64 .. 1024)
 int norm_threads_per_row(int64_t M, int H);
 

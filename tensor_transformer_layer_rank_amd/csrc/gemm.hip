@@ -162,7 +162,12 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   // B rows of this tile: [b_row0, +BN) or, for silu, [gate0, +BN/2) and [up0, +BN/2)
   const int64_t nrow0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) : (int64_t)tn * BN;
   const int64_t nrows = EPI == EPI_SILU_BF16 ? p.li - nrow0 : p.N - nrow0;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
+  // A rows: the tile's own rows from m0, or (row gather) rows a_rows[m0 + r]
+  // of the whole A, a row past M or an index outside A at an offset past
+  // the descriptor's range (2^31 + a K offset below 2^23: zeros)
+  const bool gather = !SPLIT && EPI != EPI_QKV && p.a_rows != nullptr;
+  const __amdgpu_buffer_rsrc_t ra =
+      gather ? make_rsrc(p.A, p.a_total * lda_b) : make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.B + (p.li + nrow0) * p.ldb, nrows * ldb_b);   // silu only
   // per-slice lane offsets (bytes, column 0) and LDS destinations within a stage
@@ -173,7 +178,12 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     const int g = wave + (isA ? v : v - A_G) * NW;
     const bool up = !isA && EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
     const int row = g * RPI + grow - (up ? BN / 2 : 0);
-    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + (swz<BK>(row, gpc) << 4));
+    uint32_t base = (uint32_t)(row * (isA ? lda_b : ldb_b));
+    if (isA && gather) {
+      const int64_t src = m0 + row < M ? (int64_t)p.a_rows[m0 + row] : -1;
+      base = src >= 0 && src < p.a_total ? (uint32_t)(src * lda_b) : 0x80000000u;
+    }
+    voff[v] = base + (uint32_t)(swz<BK>(row, gpc) << 4);
   }
   auto dma_slice = [&](int v, int64_t k0, int buf) {
     bf16* st = smem + buf * STAGE;
@@ -1129,12 +1139,13 @@ int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
 
 hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratch_bytes, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const bool can_split = epi != EPI_ARGMAX && scratch != nullptr && scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
+  const bool can_split = epi != EPI_ARGMAX && !p.a_rows && scratch != nullptr &&
+                         scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
   const Plan pl = make_plan(p.M, p.N, p.K, epi, can_split);
   // eight or more rounds of 256 x 256 tiles: one persistent workgroup per
   // CU (measured: faster from about that many rounds on, when the per-tile
   // fill and relaunch it saves are a visible part of a tile's time)
-  if (pl.v == V256x256 && pl.splits == 1 && epi == EPI_BF16 && (int64_t)pl.tiles_m * pl.tiles_n >= 8 * kCUs) {
+  if (pl.v == V256x256 && pl.splits == 1 && epi == EPI_BF16 && !p.a_rows && (int64_t)pl.tiles_m * pl.tiles_n >= 8 * kCUs) {
     gemm_persist_kernel<256, 256, 4, 2, EPI_BF16, 8, 2><<<kCUs, 512, 0, s>>>(p, pl.tiles_m, pl.tiles_n);
     mark_gemm(s, "gemm_persist", 256, 256, 2, EPI_BF16);
     return hipGetLastError();

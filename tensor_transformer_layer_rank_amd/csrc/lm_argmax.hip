@@ -109,8 +109,8 @@ constexpr int kResSegK = 256;                // K granularity of the head
 
 template <int MQ, int KS, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const bf16* __restrict__ vocab, int64_t N,
-                            u32x2* __restrict__ cand) {
+void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const int32_t* __restrict__ rows,
+                            int64_t x_rows, const bf16* __restrict__ vocab, int64_t N, u32x2* __restrict__ cand) {
   constexpr int K = KS * 128;                 // 4 waves x KS steps x 32
   // rows padded to 20 floats: the four 16-lane groups of a wave write rows 4
   // apart, which then start 16 banks apart instead of on the same banks
@@ -119,17 +119,24 @@ void argmax_resident_kernel(const bf16* __restrict__ x, int64_t M, const bf16* _
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int kw0 = wave * (K / 4);             // this wave's K quarter
-  // the rows' fragments of this quarter (rows past M read as zeros)
+  // the rows' fragments of this quarter: row r, or x row rows[r] with a row
+  // list; rows past M and indices outside x read as zeros (past the range)
   const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(x), (short)0, (int)(M * K * 2), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(x), (short)0, (int)((rows ? x_rows : M) * K * 2), 0x00020000);
+  uint32_t xoff[MQ];
+#pragma unroll
+  for (int i = 0; i < MQ; ++i) {
+    const int r = i * 16 + l16;
+    int64_t src = r < M ? r : -1;
+    if (rows && r < M) src = rows[r] >= 0 && rows[r] < x_rows ? rows[r] : -1;
+    xoff[i] = src >= 0 ? (uint32_t)(src * K + kw0 + g * 8) * 2u : 0x80000000u;
+  }
   bf16x8 af[KS][MQ];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int i = 0; i < MQ; ++i)
-      af[s][i] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((i * 16 + l16) * K + kw0 + s * 32 + g * 8) * 2u,
-                                                        0, 0));
+      af[s][i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + s * 64u, 0, 0));
   // this workgroup's run of whole 16-row chunks
   const int64_t nch = (N + 15) / 16;
   const int c0 = (int)(nch * blockIdx.x / gridDim.x), c1 = (int)(nch * (blockIdx.x + 1) / gridDim.x);
@@ -212,8 +219,8 @@ bool argmax_resident_ok(int64_t M, int64_t N, int64_t K) {
 
 int argmax_resident_groups() { return kCUs; }
 
-hipError_t argmax_resident(const void* x, int64_t M, const void* vocab, int64_t N, int64_t K, void* cand,
-                           hipStream_t s) {
+hipError_t argmax_resident(const void* x, int64_t M, const int32_t* rows, int64_t x_rows, const void* vocab,
+                           int64_t N, int64_t K, void* cand, hipStream_t s) {
   if (!argmax_resident_ok(M, N, K)) return hipErrorInvalidValue;
   const bf16* xb = static_cast<const bf16*>(x);
   const bf16* vb = static_cast<const bf16*>(vocab);
@@ -222,11 +229,11 @@ hipError_t argmax_resident(const void* x, int64_t M, const void* vocab, int64_t 
   auto go = [&](auto ks) {
     constexpr int KS = decltype(ks)::value;
     if (M <= 16)
-      argmax_resident_kernel<1, KS, 3><<<kCUs, 256, 0, s>>>(xb, M, vb, N, cb);
+      argmax_resident_kernel<1, KS, 3><<<kCUs, 256, 0, s>>>(xb, M, rows, x_rows, vb, N, cb);
     else if (M <= 32)
-      argmax_resident_kernel<2, KS, 3><<<kCUs, 256, 0, s>>>(xb, M, vb, N, cb);
+      argmax_resident_kernel<2, KS, 3><<<kCUs, 256, 0, s>>>(xb, M, rows, x_rows, vb, N, cb);
     else
-      argmax_resident_kernel<4, KS, 2><<<kCUs, 256, 0, s>>>(xb, M, vb, N, cb);
+      argmax_resident_kernel<4, KS, 2><<<kCUs, 256, 0, s>>>(xb, M, rows, x_rows, vb, N, cb);
   };
   switch (K) {
     case 256: go(std::integral_constant<int, 2>{}); break;

@@ -15,6 +15,11 @@
 // over the rank's token slice: plane stays the full M * H, the row pointers
 // start at the slice.  The threads of a row keep it in registers between the sum and
 // the scaling: every input byte is read once and each output written once.
+//
+// With no partials it is the plain RMSNorm, and with a row list it reads
+// input row in_rows[m] for output row m: the final norm on each sequence's
+// last position before the head ("Implementation", TPTransformer.forward
+// norms x[:, -1:]).
 #include "common.h"
 
 namespace tps {
@@ -30,47 +35,63 @@ template <int NC>
 constexpr int norm_group() { return NC == 1 ? 16 : NC == 2 ? 8 : 4; }
 
 template <int TPR, int NC>
-__global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel(
-    const bf16* __restrict__ partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
-    const bf16* __restrict__ w, float eps, bf16* h_out, bf16* __restrict__ y_out) {
+__global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel(NormArgs a) {
   constexpr int BLOCK = TPR > 256 ? TPR : 256, ROWS = BLOCK / TPR, G = norm_group<NC>();
+  const bf16* __restrict__ partials = a.partials;
+  const bf16* residual = a.residual;
+  const bf16* __restrict__ w = a.w;
+  bf16* h_out = a.h_out;
+  bf16* __restrict__ y_out = a.y_out;
+  const int n = a.n, H = a.H;
+  const int64_t plane = a.plane, M = a.M;
   const int t = threadIdx.x % TPR;
   const int64_t m = (int64_t)blockIdx.x * ROWS + threadIdx.x / TPR;
   const bool live = m < M;
   const int nc = H / 8;
   const int64_t row = (live ? m : 0) * H;
-  bool on[NC];
+  // input row: m, or in_rows[m] (outside [0, in_nrows): a zero row)
+  int64_t src = live ? m : 0;
+  bool in_ok = live;
+  if (a.in_rows && live) {
+    src = a.in_rows[m];
+    in_ok = src >= 0 && src < a.in_nrows;
+    if (!in_ok) src = 0;
+  }
+  const int64_t irow = src * H;
+  bool on[NC], ld[NC];
 #pragma unroll
-  for (int k = 0; k < NC; ++k) on[k] = live && t + k * TPR < nc;
+  for (int k = 0; k < NC; ++k) {
+    on[k] = live && t + k * TPR < nc;
+    ld[k] = on[k] && in_ok;
+  }
   // residual, norm weight and the first group of partials are all
   // requested before the first use of any of them
   bf16x8 rv[NC], wv[NC], v[G][NC];
 #pragma unroll
-  for (int k = 0; k < NC; ++k)
-    if (on[k]) {
-      rv[k] = *reinterpret_cast<const bf16x8*>(residual + row + (int64_t)(t + k * TPR) * 8);
-      wv[k] = *reinterpret_cast<const bf16x8*>(w + (int64_t)(t + k * TPR) * 8);
-    }
+  for (int k = 0; k < NC; ++k) {
+    rv[k] = bf16x8{};
+    if (ld[k]) rv[k] = *reinterpret_cast<const bf16x8*>(residual + irow + (int64_t)(t + k * TPR) * 8);
+    if (on[k]) wv[k] = *reinterpret_cast<const bf16x8*>(w + (int64_t)(t + k * TPR) * 8);
+  }
   float acc[NC][8];
+#pragma unroll
+  for (int k = 0; k < NC; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[k][e] = ld[k] ? bf2f(rv[k][e]) : 0.f;
   for (int r0 = 0; r0 < n; r0 += G) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int k = 0; k < NC; ++k)
-        if (r0 + g < n && on[k])
-          v[g][k] = *reinterpret_cast<const bf16x8*>(partials + (int64_t)(r0 + g) * plane + row +
+        if (r0 + g < n && ld[k])
+          v[g][k] = *reinterpret_cast<const bf16x8*>(partials + (int64_t)(r0 + g) * plane + irow +
                                                      (int64_t)(t + k * TPR) * 8);
-    if (r0 == 0)
-#pragma unroll
-      for (int k = 0; k < NC; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[k][e] = on[k] ? bf2f(rv[k][e]) : 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g)   // rank order
       if (r0 + g < n)
 #pragma unroll
         for (int k = 0; k < NC; ++k)
-          if (on[k])
+          if (ld[k])
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[k][e] += bf2f(v[g][k][e]);
   }
@@ -85,7 +106,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel
         acc[k][e] = bf2f(hb[e]);   // the norm sees the stored (rounded) residual
         ss += acc[k][e] * acc[k][e];
       }
-      __builtin_nontemporal_store(hb, reinterpret_cast<bf16x8*>(h_out + row + (int64_t)(t + k * TPR) * 8));
+      if (h_out) __builtin_nontemporal_store(hb, reinterpret_cast<bf16x8*>(h_out + row + (int64_t)(t + k * TPR) * 8));
     }
   }
   ss = wave_sum64(ss);
@@ -98,7 +119,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel
 #pragma unroll
     for (int i = 0; i < TPR / 64; ++i) ss += s_ss[w0 + i];
   }
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     if (on[k]) {
@@ -111,22 +132,19 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void residual_rmsnorm_kernel
 }
 
 template <int TPR, int NC>
-void launch_norm(const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual, const bf16* w,
-                 float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
+void launch_norm(const NormArgs& a, hipStream_t s) {
   constexpr int BLOCK = TPR > 256 ? TPR : 256, ROWS = BLOCK / TPR;
-  const unsigned grid = (unsigned)((M + ROWS - 1) / ROWS);
-  residual_rmsnorm_kernel<TPR, NC>
-      <<<grid, BLOCK, 0, s>>>(partials, n, plane, M, H, residual, w, eps, h_out, y_out);
+  const unsigned grid = (unsigned)((a.M + ROWS - 1) / ROWS);
+  residual_rmsnorm_kernel<TPR, NC><<<grid, BLOCK, 0, s>>>(a);
 }
 
 template <int TPR>
-void launch_norm_tpr(int nc_per, const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
-                     const bf16* w, float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
+void launch_norm_tpr(int nc_per, const NormArgs& a, hipStream_t s) {
   switch (nc_per) {
-    case 1: launch_norm<TPR, 1>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 2: launch_norm<TPR, 2>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 3: launch_norm<TPR, 3>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    default: launch_norm<TPR, 4>(partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 1: launch_norm<TPR, 1>(a, s); break;
+    case 2: launch_norm<TPR, 2>(a, s); break;
+    case 3: launch_norm<TPR, 3>(a, s); break;
+    default: launch_norm<TPR, 4>(a, s); break;
   }
 }
 
@@ -142,21 +160,21 @@ int norm_threads_per_row(int64_t M, int H) {
   return tpr;
 }
 
-hipError_t residual_rmsnorm(const bf16* partials, int n, int64_t plane, int64_t M, int H, const bf16* residual,
-                            const bf16* w, float eps, bf16* h_out, bf16* y_out, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  if (H <= 0 || H % 8 || H > 8192 || n < 1) return hipErrorInvalidValue;
-  const int nc = H / 8;   // 1..1024
-  const int tpr = norm_threads_per_row(M, H);
+hipError_t residual_rmsnorm(const NormArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.H <= 0 || a.H % 8 || a.H > 8192 || a.n < 0 || (a.n > 0 && !a.partials) || (a.n > 0 && !a.h_out))
+    return hipErrorInvalidValue;
+  const int nc = a.H / 8;   // 1..1024
+  const int tpr = norm_threads_per_row(a.M, a.H);
   const int per = (nc + tpr - 1) / tpr;   // 1..4
   switch (tpr) {
-    case 64: launch_norm_tpr<64>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 128: launch_norm_tpr<128>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 256: launch_norm_tpr<256>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    case 512: launch_norm_tpr<512>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
-    default: launch_norm_tpr<1024>(per, partials, n, plane, M, H, residual, w, eps, h_out, y_out, s); break;
+    case 64: launch_norm_tpr<64>(per, a, s); break;
+    case 128: launch_norm_tpr<128>(per, a, s); break;
+    case 256: launch_norm_tpr<256>(per, a, s); break;
+    case 512: launch_norm_tpr<512>(per, a, s); break;
+    default: launch_norm_tpr<1024>(per, a, s); break;
   }
-  kmark(s, "residual_rmsnorm");
+  kmark(s, a.in_rows ? "rmsnorm_rows" : a.n ? "residual_rmsnorm" : "rmsnorm");
   return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <string>
 #include <vector>
 
@@ -133,6 +134,40 @@ LmWs lm_ws(const tp_cfg* c, const tp_local& L, int64_t M) {
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
+
+// the optional row list of the heads: rows_opt NULL (x rows 0..M-1) or an
+// int32 list into x's x_rows rows, read through one 31-bit descriptor range
+int check_head_rows(const tp_cfg* cfg, int64_t M, const int32_t* rows, int64_t x_rows) {
+  if (!rows) return TP_OK;
+  if (x_rows < 1) return TP_ERR_RANGE;
+  if ((uintptr_t)rows & 3) return TP_ERR_ALIGN;
+  if (x_rows * cfg->hidden * 2 >= ((int64_t)1 << 31)) return TP_ERR_SHAPE;
+  (void)M;
+  return TP_OK;
+}
+
+// the decode head's launches: per-shard candidates into `cand` (w.total
+// bytes), then their reduction to one (value, id) per row
+hipError_t lm_head_argmax_launch(const tp_cfg* cfg, const tp_local& L, const void* x, int64_t M, const int32_t* rows,
+                                 int64_t x_rows, const void* vocab_local, float* out_val, int32_t* out_idx,
+                                 const LmWs& w, void* cand, hipStream_t s) {
+  const int64_t N = L.vocab_end - L.vocab_start, H = cfg->hidden;
+  if (w.resident) {
+    // few rows, short hidden size: rows resident on chip, the vocab slice
+    // streamed once
+    const hipError_t e = argmax_resident(x, M, rows, x_rows, vocab_local, N, H, cand, s);
+    if (e != hipSuccess) return e;
+  } else if (N > 0) {
+    // logits GEMM whose epilogue leaves one candidate per row and N tile
+    GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), cand, M, N, H, H, H,
+                  w.tiles_n, 0};
+    g.a_rows = rows;
+    g.a_total = x_rows;
+    const hipError_t e = gemm_bf16(g, EPI_ARGMAX, nullptr, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  return argmax_candidates(cand, M, w.tiles_n, L.vocab_start, out_val, out_idx, s);
+}
 
 // The kernels read through buffer descriptors whose byte range is 32-bit.
 // A GEMM tile's descriptor starts at the tile's first row and its loads
@@ -370,8 +405,8 @@ int tp_mlp(const tp_cfg* cfg, const void* x, int64_t M, const void* w_gate_up, c
   return launched(gemm_bf16(gd, EPI_BF16, scratch, w.scratch_bytes, s));
 }
 
-int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local, void* logits_local,
-               void* stream) {
+int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const int32_t* rows_opt, int64_t x_rows,
+               const void* vocab_local, void* logits_local, void* stream) {
   tp_local L;
   int st = check_cfg(cfg, &L);
   if (st) return st;
@@ -379,6 +414,8 @@ int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_lo
   if (M < 0) return TP_ERR_RANGE;
   if (!x || !vocab_local || !logits_local) return TP_ERR_NULL;
   if (!aligned16(x) || !aligned16(vocab_local) || !aligned16(logits_local)) return TP_ERR_ALIGN;
+  if ((st = check_head_rows(cfg, M, rows_opt, x_rows))) return st;
+  if (rows_opt && cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
   const int64_t N = L.vocab_end - L.vocab_start, H = cfg->hidden;
   if (M == 0 || N == 0) return TP_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -386,11 +423,14 @@ int tp_lm_head(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_lo
     return launched(gemm_f32(static_cast<const float*>(x), static_cast<const float*>(vocab_local),
                              static_cast<float*>(logits_local), M, N, H, 0, s));
   GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), logits_local, M, N, H, H, H, N, 0};
+  g.a_rows = rows_opt;
+  g.a_total = x_rows;
   return launched(gemm_bf16(g, EPI_BF16, nullptr, 0, s));
 }
 
-int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* vocab_local, float* out_val,
-                      int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
+int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const int32_t* rows_opt, int64_t x_rows,
+                      const void* vocab_local, float* out_val, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                      void* stream) {
   tp_local L;
   int st = check_cfg(cfg, &L);
   if (st) return st;
@@ -400,6 +440,7 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* v
   if (!x || !vocab_local || !out_val || !out_idx) return TP_ERR_NULL;
   if (!aligned16(x) || !aligned16(vocab_local) || ((uintptr_t)out_val & 3) || ((uintptr_t)out_idx & 3))
     return TP_ERR_ALIGN;
+  if ((st = check_head_rows(cfg, M, rows_opt, x_rows))) return st;
   if (M == 0) return TP_OK;
   const LmWs w = lm_ws(cfg, L, M);
   if (w.total > 0) {
@@ -407,20 +448,8 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const void* v
     if (!aligned16(workspace)) return TP_ERR_ALIGN;
     if (ws_bytes < w.total) return TP_ERR_WORKSPACE;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t N = L.vocab_end - L.vocab_start, H = cfg->hidden;
-  if (w.resident) {
-    // few rows, short hidden size: rows resident in LDS, the vocab slice
-    // streamed once
-    if (argmax_resident(x, M, vocab_local, N, H, workspace, s) != hipSuccess) return TP_ERR_LAUNCH;
-  } else if (N > 0) {
-    // logits GEMM whose epilogue leaves one candidate per row and N tile
-    GemmProblem g{static_cast<const bf16*>(x), static_cast<const bf16*>(vocab_local), workspace, M, N, H, H, H,
-                  w.tiles_n, 0};
-    const hipError_t e = gemm_bf16(g, EPI_ARGMAX, nullptr, 0, s);
-    if (e != hipSuccess) return TP_ERR_LAUNCH;
-  }
-  return launched(argmax_candidates(workspace, M, w.tiles_n, L.vocab_start, out_val, out_idx, s));
+  return launched(lm_head_argmax_launch(cfg, L, x, M, rows_opt, x_rows, vocab_local, out_val, out_idx, w, workspace,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, int64_t M, int32_t* out_idx,
@@ -439,16 +468,48 @@ int tp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int32_t n_parti
   if (st) return st;
   if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
   if (cfg->hidden % 8 || cfg->hidden > 8192) return TP_ERR_SHAPE;
-  if (n_partials < 1 || M < 0) return TP_ERR_RANGE;
-  if (!partials || !residual || !norm_w || !h_out || !y_out) return TP_ERR_NULL;
+  if (n_partials < 0 || M < 0) return TP_ERR_RANGE;
+  if ((n_partials > 0 && (!partials || !h_out)) || !residual || !norm_w || !y_out) return TP_ERR_NULL;
   const void* ptrs[] = {partials, residual, norm_w, h_out, y_out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return TP_ERR_ALIGN;
   if (M == 0) return TP_OK;
-  return launched(residual_rmsnorm(static_cast<const bf16*>(partials), n_partials, M * cfg->hidden, M, cfg->hidden,
-                                   static_cast<const bf16*>(residual), static_cast<const bf16*>(norm_w),
-                                   cfg->rms_eps, static_cast<bf16*>(h_out), static_cast<bf16*>(y_out),
-                                   static_cast<hipStream_t>(stream)));
+  NormArgs a{static_cast<const bf16*>(partials), n_partials, M * cfg->hidden, M, cfg->hidden,
+             static_cast<const bf16*>(residual), static_cast<const bf16*>(norm_w), cfg->rms_eps,
+             static_cast<bf16*>(h_out), static_cast<bf16*>(y_out), nullptr, M};
+  return launched(residual_rmsnorm(a, static_cast<hipStream_t>(stream)));
+}
+
+int tp_rmsnorm_rows(const tp_cfg* cfg, const void* x, int64_t x_rows, const int32_t* rows, int64_t n_rows,
+                    const void* norm_w, void* y_out, void* stream) {
+  int st = check_cfg(cfg, nullptr);
+  if (st) return st;
+  if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (cfg->hidden % 8 || cfg->hidden > 8192) return TP_ERR_SHAPE;
+  if (x_rows < 0 || n_rows < 0 || (!rows && n_rows > x_rows) || (rows && n_rows > 0 && x_rows < 1)) return TP_ERR_RANGE;
+  if (n_rows == 0) return TP_OK;
+  if (!x || !norm_w || !y_out) return TP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(norm_w) || !aligned16(y_out) || ((uintptr_t)rows & 3)) return TP_ERR_ALIGN;
+  NormArgs a{nullptr, 0, 0, n_rows, cfg->hidden, static_cast<const bf16*>(x), static_cast<const bf16*>(norm_w),
+             cfg->rms_eps, nullptr, static_cast<bf16*>(y_out), rows, rows ? x_rows : n_rows};
+  return launched(residual_rmsnorm(a, static_cast<hipStream_t>(stream)));
+}
+
+int tp_last_token_rows(const int32_t* seq_lens, int32_t n_seqs, int32_t* rows_out) {
+  if (n_seqs < 0) return TP_ERR_RANGE;
+  if (n_seqs > 0 && (!seq_lens || !rows_out)) return TP_ERR_NULL;
+  int64_t end = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    if (seq_lens[b] < 1) return TP_ERR_RANGE;
+    end += seq_lens[b];
+    if (end - 1 > INT32_MAX) return TP_ERR_SHAPE;
+  }
+  end = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    end += seq_lens[b];
+    rows_out[b] = (int32_t)(end - 1);
+  }
+  return TP_OK;
 }
 
 int tp_sp_rows(const tp_cfg* cfg, int64_t M, int64_t* row0, int64_t* row1) {
@@ -475,10 +536,10 @@ int tp_sp_residual_rmsnorm(const tp_cfg* cfg, const void* partials, int64_t M, c
   for (const void* p : ptrs)
     if (!aligned16(p)) return TP_ERR_ALIGN;
   const int64_t H = cfg->hidden;
-  return launched(residual_rmsnorm(static_cast<const bf16*>(partials) + r0 * H, cfg->tp_size, M * H, r1 - r0,
-                                   cfg->hidden, static_cast<const bf16*>(residual_slice),
-                                   static_cast<const bf16*>(norm_w), cfg->rms_eps, static_cast<bf16*>(h_slice_out),
-                                   static_cast<bf16*>(y_gathered) + r0 * H, static_cast<hipStream_t>(stream)));
+  NormArgs a{static_cast<const bf16*>(partials) + r0 * H, cfg->tp_size, M * H, r1 - r0, cfg->hidden,
+             static_cast<const bf16*>(residual_slice), static_cast<const bf16*>(norm_w), cfg->rms_eps,
+             static_cast<bf16*>(h_slice_out), static_cast<bf16*>(y_gathered) + r0 * H, nullptr, r1 - r0};
+  return launched(residual_rmsnorm(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

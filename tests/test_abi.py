@@ -118,6 +118,10 @@ class Fake:
     def element_size(self):
         return self.es
 
+    @property
+    def shape(self):
+        return (self.n,)
+
 
 class NullStream:
     cuda_stream = 0
@@ -233,7 +237,11 @@ def test_residual_rmsnorm_validation():
     c = tp.Cfg(hidden=256, tp_size=2)
     assert _status(tp.tp_residual_rmsnorm, c, A, 2, 0, A, A, A, A, s) == OK             # M = 0
     assert _status(tp.tp_residual_rmsnorm, c, A, 2, -1, A, A, A, A, s) == E_RANGE
-    assert _status(tp.tp_residual_rmsnorm, c, A, 0, 5, A, A, A, A, s) == E_RANGE        # no partials
+    assert _status(tp.tp_residual_rmsnorm, c, A, -1, 5, A, A, A, A, s) == E_RANGE       # negative count
+    assert _status(tp.tp_residual_rmsnorm, c, None, 0, 0, A, A, None, A, s) == OK       # plain norm, M = 0
+    assert _status(tp.tp_residual_rmsnorm, c, None, 1, 5, A, A, A, A, s) == E_NULL      # partials needed
+    assert _status(tp.tp_residual_rmsnorm, c, A, 1, 5, A, A, None, A, s) == E_NULL      # h_out needed
+    assert _status(tp.tp_residual_rmsnorm, c, None, 0, 5, A, A, None, None, s) == E_NULL
     assert _status(tp.tp_residual_rmsnorm, c, A, 2, 5, None, A, A, A, s) == E_NULL
     assert _status(tp.tp_residual_rmsnorm, c, A, 2, 5, A, A, A, None, s) == E_NULL
     assert _status(tp.tp_residual_rmsnorm, c, A, 2, 5, A, A, MIS, A, s) == E_ALIGN
@@ -296,3 +304,34 @@ def test_descriptor_range_limits():
     cv = tp.Cfg(hidden=big, vocab=1000, tp_size=2)
     assert _status(tp.tp_lm_head, cv, A, 4, A, A, s) == E_SHAPE
     assert _status(tp.tp_lm_head_argmax, cv, A, 4, A, A, A, ws, s) == E_SHAPE
+
+
+@host_only
+def test_rmsnorm_rows_and_head_rows_validation():
+    s = NullStream()
+    c = tp.Cfg(hidden=256, tp_size=2)
+    assert _status(tp.tp_rmsnorm_rows, c, A, A, 0, A, A, s) == OK                 # n_rows = 0
+    assert _status(tp.tp_rmsnorm_rows, c, A, A, -1, A, A, s) == E_RANGE
+    assert _status(tp.tp_rmsnorm_rows, c, Fake(1 << 40), None, 5, A, A, s) == E_RANGE    # 5 rows of a 0-row x
+    assert _status(tp.tp_rmsnorm_rows, c, Fake(1 << 40, 9), Fake((1 << 40) + 2), 5, A, A, s) == E_ALIGN
+    assert _status(tp.tp_rmsnorm_rows, c, A, A, 5, A, A, s) == E_RANGE                  # row list, 0-row x
+    assert _status(tp.tp_rmsnorm_rows, c, Fake(1 << 40, 9), A, 5, A, None, s) == E_NULL
+    assert _status(tp.tp_rmsnorm_rows, tp.Cfg(hidden=260, tp_size=2), A, A, 5, A, A, s) == E_SHAPE
+    assert _status(tp.tp_rmsnorm_rows, tp.Cfg(hidden=256, tp_size=2, dtype=tp.TP_F32), A, A, 5, A, A, s) == E_DTYPE
+    cv = tp.Cfg(hidden=256, vocab=1000, tp_size=4, tp_rank=1)
+    ws = Fake(1 << 40, 1 << 20, 1)
+    lib = tp.lib()
+    assert lib.tp_lm_head(cv.c(), A.addr, 4, (1 << 40) + 2, 8, A.addr, A.addr, None) == E_ALIGN
+    assert lib.tp_lm_head(cv.c(), A.addr, 4, 1 << 40, 0, A.addr, A.addr, None) == E_RANGE
+    assert lib.tp_lm_head(cv.c(), A.addr, 4, 1 << 40, 1 << 22, A.addr, A.addr, None) == E_SHAPE   # 2 GiB of rows
+    assert lib.tp_lm_head_argmax(cv.c(), A.addr, 4, 1 << 40, 0, A.addr, A.addr, A.addr, ws.addr, ws.n, None) == E_RANGE
+    cf = tp.Cfg(hidden=256, vocab=1000, tp_size=4, dtype=tp.TP_F32)
+    assert lib.tp_lm_head(cf.c(), A.addr, 4, 1 << 40, 8, A.addr, A.addr, None) == E_DTYPE
+
+
+def test_last_token_rows():
+    assert tp.tp_last_token_rows([5, 5, 5]) == list(O.last_token_rows([5, 5, 5]))
+    assert tp.tp_last_token_rows([3, 1, 7, 2]) == list(O.last_token_rows([3, 1, 7, 2]))
+    assert tp.tp_last_token_rows([]) == []
+    assert _status(tp.tp_last_token_rows, [2, 0]) == E_RANGE
+    assert _status(tp.tp_last_token_rows, [1 << 30, 1 << 30, 1 << 30]) == E_SHAPE
