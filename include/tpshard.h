@@ -263,6 +263,24 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const int32_t
                       const void* vocab_local, float* out_val, int32_t* out_idx, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* tp_lm_head_argmax_noalloc -- tp_lm_head_argmax for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments and
+ * results as tp_lm_head_argmax minus the workspace: the per-row partial
+ * candidates go to a static device array of 4 MiB inside the library (one
+ * per GPU, held until the process ends), so the call allocates nothing.
+ * Limit: the candidates of M rows must fit it, i.e. the bytes
+ * tp_workspace_bytes(cfg, TP_OP_LM_ARGMAX, M, 1, 0) reports must be at most
+ * 4 MiB (TP_ERR_WORKSPACE otherwise; e.g. 64 rows on the on-chip path, or
+ * 512 rows of a 75968-row vocab slice, fit).  The array is
+ * looked up on the current device (hipGetDevice): `stream` must belong to
+ * it.  Every call on one GPU shares that GPU's array, so calls that overlap
+ * on one GPU (on different streams, or from several host threads) race;
+ * calls on one stream are ordered and safe.  Nothing in the array needs
+ * clearing: each call writes every slot it reads. */
+int tp_lm_head_argmax_noalloc(const tp_cfg* cfg, const void* x, int64_t M, const int32_t* rows_opt, int64_t x_rows,
+                              const void* vocab_local, float* out_val, int32_t* out_idx, void* stream);
+
 /* tp_argmax_combine -- the cross-shard step of the greedy argmax: per row the
  * candidate with the largest value, ties to the smallest token id (the first
  * maximum of the concatenated logits, as argmax takes it); candidates with

@@ -22,8 +22,8 @@ TP_OP_ATTN, TP_OP_MLP, TP_OP_LM_ARGMAX = 0, 1, 2
 
 EXPORTS = ("tp_local_dims", "tp_workspace_bytes", "tp_status_str", "tp_kernel_marks", "tp_kernel_marks_used",
            "tp_kernel_mark_name", "tp_shard_weights", "tp_embed_vocab", "tp_qkv_attn", "tp_mlp", "tp_lm_head",
-           "tp_lm_head_argmax", "tp_argmax_combine", "tp_residual_rmsnorm", "tp_rmsnorm_rows", "tp_last_token_rows",
-           "tp_sp_rows", "tp_sp_residual_rmsnorm")
+           "tp_lm_head_argmax", "tp_lm_head_argmax_noalloc", "tp_argmax_combine", "tp_residual_rmsnorm",
+           "tp_rmsnorm_rows", "tp_last_token_rows", "tp_sp_rows", "tp_sp_residual_rmsnorm")
 
 
 class TpError(RuntimeError):
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp.argtypes = [C, P, I64, P, P, P, P, P, SZ, P]
         L.tp_lm_head.argtypes = [C, P, I64, P, I64, P, P, P]
         L.tp_lm_head_argmax.argtypes = [C, P, I64, P, I64, P, P, P, P, SZ, P]
+        L.tp_lm_head_argmax_noalloc.argtypes = [C, P, I64, P, I64, P, P, P, P]
         L.tp_argmax_combine.argtypes = [P, P, I32, I64, P, P, P]
         L.tp_residual_rmsnorm.argtypes = [C, P, I32, I64, P, P, P, P, P]
         L.tp_rmsnorm_rows.argtypes = [C, P, I64, P, I64, P, P, P]
@@ -215,6 +216,13 @@ def tp_lm_head_argmax(cfg: Cfg, x, M: int, vocab_local, out_val, out_idx, worksp
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().tp_lm_head_argmax(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(rows), _x_rows(x, rows), _ptr(vocab_local),
                                    _ptr(out_val), _ptr(out_idx), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_lm_head_argmax_noalloc(cfg: Cfg, x, M: int, vocab_local, out_val, out_idx, stream=None, rows=None):
+    """tp_lm_head_argmax with its candidates in the library's static device
+    array: no workspace, no allocation."""
+    _check(lib().tp_lm_head_argmax_noalloc(ctypes.byref(cfg.c()), _ptr(x), M, _ptr(rows), _x_rows(x, rows),
+                                           _ptr(vocab_local), _ptr(out_val), _ptr(out_idx), _stream(stream)))
 
 
 def tp_argmax_combine(vals, idx, n_shards: int, M: int, out_idx, out_val=None, stream=None):

@@ -227,6 +227,10 @@ int argmax_resident_groups();
 // zeros), with x_rows * K * 2 < 2^31
 hipError_t argmax_resident(const void* x, int64_t M, const int32_t* rows, int64_t x_rows, const void* vocab,
                            int64_t N, int64_t K, void* cand, hipStream_t s);
+// Device address, on the current device, of the library's static candidate
+// array of kNoAllocScratchBytes (looked up once per device; no allocation).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** ptr);
 // out_idx[m] = the candidate (vals, idx [n_shards, M]) with the largest
 // value, ties to the smallest index, idx < 0 skipped; out_val optional.
 hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, int64_t M, int32_t* out_idx,

@@ -13,6 +13,7 @@
 // argmax_pairs: one workgroup per row reduces the row's candidates (a
 // per-thread best, then wave shuffles and LDS).  combine_candidates: one
 // thread per row over the ranks.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -251,6 +252,35 @@ hipError_t argmax_candidates(const void* cand, int64_t M, int64_t n, int64_t idx
   argmax_pairs<<<(unsigned)M, 256, 0, s>>>(static_cast<const u32x2*>(cand), n, idx0, out_val, out_idx);
   kmark(s, "argmax_pairs");
   return hipGetLastError();
+}
+
+// ---- the decode head's candidates without an allocation --------------------
+// A file-scope device array holds the candidates for callers that cannot
+// allocate (graph capture, tight serving loops).  In host code `scratch`
+// names a host-side stand-in, not the device copy: its device address is
+// looked up once per device with that device current, and only that address
+// is handed to kernels.  Every call on a device shares the device's array.
+namespace {
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t argmax_combine(const float* vals, const int32_t* idx, int n_shards, int64_t M, int32_t* out_idx,

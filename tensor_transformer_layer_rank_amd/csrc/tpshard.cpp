@@ -452,6 +452,27 @@ int tp_lm_head_argmax(const tp_cfg* cfg, const void* x, int64_t M, const int32_t
                                         static_cast<hipStream_t>(stream)));
 }
 
+int tp_lm_head_argmax_noalloc(const tp_cfg* cfg, const void* x, int64_t M, const int32_t* rows_opt, int64_t x_rows,
+                              const void* vocab_local, float* out_val, int32_t* out_idx, void* stream) {
+  tp_local L;
+  int st = check_cfg(cfg, &L);
+  if (st) return st;
+  if (cfg->dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (cfg->vocab == 0 || cfg->hidden % 8 || !row_ok(cfg->hidden)) return TP_ERR_SHAPE;
+  if (M < 0) return TP_ERR_RANGE;
+  if (!x || !vocab_local || !out_val || !out_idx) return TP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(vocab_local) || ((uintptr_t)out_val & 3) || ((uintptr_t)out_idx & 3))
+    return TP_ERR_ALIGN;
+  if ((st = check_head_rows(cfg, M, rows_opt, x_rows))) return st;
+  if (M == 0) return TP_OK;
+  const LmWs w = lm_ws(cfg, L, M);
+  if (w.total > kNoAllocScratchBytes) return TP_ERR_WORKSPACE;   // candidates exceed the static array
+  void* cand = nullptr;
+  if (noalloc_scratch(&cand) != hipSuccess) return TP_ERR_LAUNCH;
+  return launched(lm_head_argmax_launch(cfg, L, x, M, rows_opt, x_rows, vocab_local, out_val, out_idx, w, cand,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int tp_argmax_combine(const float* vals, const int32_t* idx, int32_t n_shards, int64_t M, int32_t* out_idx,
                       float* out_val_opt, void* stream) {
   if (n_shards < 1 || M < 0) return TP_ERR_RANGE;
