@@ -119,8 +119,11 @@ def run_mlp(rk, x, M):
 
 # ------------------------------------------------------------------ shards and embedding
 
-@pytest.mark.parametrize("name", list(MID) + ["w2", "w5"])
+@pytest.mark.parametrize("name", list(MID) + ["w2", "w4", "w5"])
 def test_shard_weights_bit_exact(name):
+    """Every weight kind, merged, bit for bit against the oracle's shard +
+    merge.  w4 (32B tp=2: 42 MB q / o shards, 131 MB gate / up / down shards)
+    takes the copy kernel's grid-stride path, which strides 32 MB a pass."""
     if name in MID:
         w, wid = MID[name], MID_WID[name]
     else:
@@ -138,6 +141,25 @@ def test_shard_weights_bit_exact(name):
         assert np.array_equal(bits16(rk.gu), gu), (name, r, "gate_up")
         assert np.array_equal(bits16(rk.o), o), (name, r, "o")
         assert np.array_equal(bits16(rk.down), down), (name, r, "down")
+
+
+@pytest.mark.parametrize("H", [1024, 5120])
+def test_vocab_shard_whole_slice_bit_exact(H):
+    """The whole vocab slice of both ranks (151936 rows over 2: 155.6 MB at
+    hidden 1024, 777.9 MB at 5120, several grid-stride passes of the copy)
+    bit for bit against the oracle's rows."""
+    V = 151936
+    E = _big_vocab(V, H)
+    Eg = E.to(DEV)
+    Eb = E.view(torch.int16).numpy()
+    for r in range(2):
+        c = tp.Cfg(hidden=H, vocab=V, tp_size=2, tp_rank=r)
+        L = tp.tp_local_dims(c)
+        dst = torch.empty(L.vocab_end - L.vocab_start, H, dtype=torch.bfloat16, device=DEV)
+        tp.tp_shard_weights(c, tp.TP_W_VOCAB, Eg, dst)
+        ref = O.shard(O.Cfg(hidden=H, vocab=V, tp_size=2, tp_rank=r), O.W_VOCAB, Eb)
+        assert np.array_equal(bits16(dst), ref), (H, r)
+        del dst
 
 
 def test_shard_weights_fp32_and_vocab():
@@ -439,6 +461,35 @@ def test_qkv_attn_mid(name, phase):
                          "decode-long": (2, 1, 2999, 3000)}[phase]
     for r in range(w["tp"]):
         check_attn(w, wid, r, B, T, past, S_max, Wg=Wg, W=W)
+
+
+@pytest.mark.parametrize("name", ["rep1", "rep2", "rep4-replicated", "rep8", "rep16"])
+@pytest.mark.parametrize("past", [0, 37])
+def test_qkv_attn_gqa_prefill_kernel(name, past):
+    """Prefills wide enough that the GQA-sharing prefill kernel runs (its
+    (kv head, row block) workgroups alone fill the GPU), at every group size
+    (rep 1, 2, 4 with a replicated kv head, 8, 16), from an empty cache and
+    after 37 cached positions (the causal offset of its row blocks).  The
+    kernel marks confirm which attention kernel ran."""
+    w, wid = MID[name], MID_WID[name]
+    W = synth.full_weights(wid, w)
+    Wg = {k: v.to(DEV) for k, v in W.items()}
+    # (kv head, row block) workgroups: B * lkv * head groups * ceil(T / rows)
+    # >= 256 with 333 tokens (128-row blocks for rep 1 and 2, 32 for 8 and 16)
+    B = {"rep1": 48, "rep2": 48, "rep4-replicated": 96, "rep8": 24, "rep16": 24}[name]
+    T = 333
+    S_max = past + T + 3
+    rows = np.unique(np.concatenate([[0, 31, 32, T - 1, T, B * T - 1],
+                                     np.random.default_rng(past + len(name)).integers(0, B * T, 24)]))
+    for r in range(w["tp"]):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(32)]
+        tp.tp_kernel_marks(ev)
+        try:
+            check_attn(w, wid, r, B, T, past, S_max, rows=rows, Wg=Wg, W=W)
+            names = tp.tp_kernel_mark_names()
+        finally:
+            tp.tp_kernel_marks([])
+        assert "attn_prefill" in names, names
 
 
 def test_qkv_attn_row_sum_and_head_concat():
