@@ -140,6 +140,7 @@ struct QkvArgs {
   bf16* v_cache;
   int B, T, past, S_max, lq, lkv;
   float eps, theta;
+  int head0;             // head of column 0 (a problem restricted to later columns)
 };
 
 struct GemmProblem {
@@ -155,6 +156,8 @@ struct GemmProblem {
   // must be below 2^31.  Never used with EPI_QKV or a split plan.
   const int32_t* a_rows;
   int64_t a_total;
+  // EPI_SILU_BF16: rows from a gate row to its up row (0: li)
+  int64_t up_off;
 };
 
 // Chooses a tile shape and launches.  When the grid would not fill the GPU

@@ -69,6 +69,7 @@ __device__ __forceinline__ void wait_vm() {
 // x[0..3] hold d = 4j .. 4j+3 of (row m, head h), x[4..7] hold d + 64
 __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
                                            const RopeCoef& rc) {
+  h += a.head0;
   const int b = (int)(m / a.T), t = (int)(m - (int64_t)b * a.T);
   const int pos = a.past + t;
   if (h < a.lq + a.lkv) qk_norm_rope(x, h < a.lq ? a.q_norm_w : a.k_norm_w, pos, j, rc, a.eps);
@@ -169,7 +170,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   const __amdgpu_buffer_rsrc_t ra =
       gather ? make_rsrc(p.A, p.a_total * lda_b) : make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
-  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.B + (p.li + nrow0) * p.ldb, nrows * ldb_b);   // silu only
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.B + ((p.up_off ? p.up_off : p.li) + nrow0) * p.ldb, nrows * ldb_b);
   // per-slice lane offsets (bytes, column 0) and LDS destinations within a stage
   uint32_t voff[NV];
 #pragma unroll
@@ -607,7 +608,7 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     const int64_t nrows = EPI == EPI_SILU_BF16 ? p.li - nrow0 : p.N - nrow0;
     ra = make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
     rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
-    ru = make_rsrc(p.B + (p.li + nrow0) * p.ldb, nrows * ldb_b);
+    ru = make_rsrc(p.B + ((p.up_off ? p.up_off : p.li) + nrow0) * p.ldb, nrows * ldb_b);
   };
   int dj = 0, dkb = 0;                    // tile and K block of the next load
   auto dma_next = [&](int buf) __attribute__((always_inline)) {
@@ -1121,15 +1122,78 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
+// ---- last-round tail ---------------------------------------------------------
+// When a plan's tiles fill whole rounds of resident workgroups plus at most
+// half a round more, that last round would leave most CUs idle.  The
+// columns of the whole rounds then run as one launch and the remaining
+// columns as a problem of their own, with a plan chosen for that shape
+// (smaller tiles, or split K).
+struct Schedule {
+  Plan main;
+  int64_t c_split;   // first output column of the tail (0: no tail)
+  Plan tail;
+};
+
+Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool gathered) {
+  Schedule sc{make_plan(M, N, K, epi, allow_split), 0, Plan{}};
+  const Plan& pl = sc.main;
+  if (pl.splits != 1 || gathered || !(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV)) return sc;
+  const Variant& v = kVariants[pl.v];
+  const int64_t R = (int64_t)kCUs * v.resident;
+  const int64_t T = (int64_t)pl.tiles_m * pl.tiles_n;
+  if (pl.v == V256x256 && epi == EPI_BF16 && T >= 8 * kCUs) return sc;   // persistent kernel
+  const int64_t full = T / R * R;
+  if (full == 0 || full == T || full % pl.tiles_m || (T - full) * 2 > R) return sc;
+  const int64_t bn_out = epi == EPI_SILU_BF16 ? v.bn / 2 : v.bn;
+  const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;
+  const int64_t c_split = full / pl.tiles_m * bn_out;
+  if (c_split >= ncols) return sc;
+  sc.c_split = c_split;
+  sc.main.tiles_n = (int)(full / pl.tiles_m);
+  const int64_t n2 = epi == EPI_SILU_BF16 ? 2 * (ncols - c_split) : ncols - c_split;
+  // a SiLU tail has its gate and up rows apart: it never splits K
+  sc.tail = make_plan(M, n2, K, epi, allow_split && epi != EPI_SILU_BF16);
+  return sc;
+}
+
+// output columns [c0, c1) of p as a problem of its own
+GemmProblem col_slice(const GemmProblem& p, int epi, int64_t c0, int64_t c1) {
+  GemmProblem q = p;
+  q.B = p.B + c0 * p.ldb;
+  if (epi == EPI_SILU_BF16) {
+    q.up_off = p.up_off ? p.up_off : p.li;
+    q.li = c1 - c0;
+    q.N = 2 * (c1 - c0);
+    q.C = static_cast<bf16*>(p.C) + c0;
+  } else if (epi == EPI_QKV) {
+    q.N = c1 - c0;
+    q.qkv.head0 = p.qkv.head0 + (int)(c0 / 128);
+  } else {
+    q.N = c1 - c0;
+    q.C = static_cast<bf16*>(p.C) + c0;
+  }
+  return q;
+}
+
+size_t split_bytes(const Plan& pl, int64_t M, int64_t N) {
+  return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+}
+
 }  // namespace
 
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int epi) {
   if (M <= 0 || N <= 0 || epi == EPI_ARGMAX) return 0;
-  int64_t splits = make_plan(M, N, K, epi, true).splits;
+  const Schedule sc = make_schedule(M, N, K, epi, true, false);
+  size_t b = split_bytes(sc.main, M, N);
+  if (sc.c_split) {
+    const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;
+    const int64_t n2 = epi == EPI_SILU_BF16 ? 2 * (ncols - sc.c_split) : ncols - sc.c_split;
+    b = std::max(b, split_bytes(sc.tail, M, n2));
+  }
   // the QKV projection may also run with its partials summed by the decode
   // attention, which can prefer more splits
-  if (epi == EPI_QKV) splits = std::max<int64_t>(splits, make_plan(M, N, K, epi, true, true).splits);
-  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+  if (epi == EPI_QKV) b = std::max(b, split_bytes(make_plan(M, N, K, epi, true, true), M, N));
+  return b;
 }
 
 int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
@@ -1137,11 +1201,30 @@ int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
   return make_plan(M, N, K, EPI_ARGMAX, false).tiles_n;
 }
 
+namespace {
+
+hipError_t launch_plan(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s,
+                       bool finish = true) {
+  switch (pl.v) {
+    case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, epi, pl, scratch, s, finish);
+    case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, epi, pl, scratch, s, finish);
+    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, epi, pl, scratch, s, finish);
+    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, epi, pl, scratch, s, finish);
+    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, epi, pl, scratch, s, finish);
+    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s, finish);
+    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s, finish);
+    default: return launch_tile<64, 64, 2, 2, 8>(p, epi, pl, scratch, s, finish);
+  }
+}
+
+}  // namespace
+
 hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratch_bytes, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const bool can_split = epi != EPI_ARGMAX && !p.a_rows && scratch != nullptr &&
                          scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
-  const Plan pl = make_plan(p.M, p.N, p.K, epi, can_split);
+  const Schedule sc = make_schedule(p.M, p.N, p.K, epi, can_split, p.a_rows != nullptr);
+  const Plan& pl = sc.main;
   // eight or more rounds of 256 x 256 tiles: one persistent workgroup per
   // CU (measured: faster from about that many rounds on, when the per-tile
   // fill and relaunch it saves are a visible part of a tile's time)
@@ -1150,16 +1233,11 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
     mark_gemm(s, "gemm_persist", 256, 256, 2, EPI_BF16);
     return hipGetLastError();
   }
-  switch (pl.v) {
-    case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, epi, pl, scratch, s);
-    case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, epi, pl, scratch, s);
-    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, epi, pl, scratch, s);
-    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, epi, pl, scratch, s);
-    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, epi, pl, scratch, s);
-    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s);
-    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s);
-    default: return launch_tile<64, 64, 2, 2, 8>(p, epi, pl, scratch, s);
-  }
+  if (!sc.c_split) return launch_plan(p, epi, pl, scratch, s);
+  const int64_t ncols = epi == EPI_SILU_BF16 ? p.li : p.N;
+  const hipError_t e = launch_plan(col_slice(p, epi, 0, sc.c_split), epi, pl, scratch, s);
+  if (e != hipSuccess) return e;
+  return launch_plan(col_slice(p, epi, sc.c_split, ncols), epi, sc.tail, scratch, s);
 }
 
 hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, bool defer, int* splits_out,
