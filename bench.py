@@ -26,9 +26,11 @@ head: the KV stream) and the vocab-parallel embedding + lm_head of
 Qwen3-0.6B at tp=2 (4096 ids, vocab 151936).
 
 Timing: HIP events on the launch stream (torch's current stream, which the
-binding passes to every call) bracket each phase, and the library's
-per-kernel marks (tp_kernel_marks) record an event after every kernel, so
-each kernel's average duration is measured live.  Inputs are synthetic,
+binding passes to every call) bracket each phase of the K timed steps; then
+K more steps run with the library's per-kernel marks (tp_kernel_marks), an
+event after every kernel, which gives each kernel's average duration (the
+marks add an event-record gap of a few microseconds at each kernel
+boundary, so the phase times come from the unmarked steps).  Inputs are synthetic,
 seeded and resident in HBM before timing; buffer sets are rotated so that
 the working set between two uses of a buffer exceeds the 256 MB Infinity
 Cache.  Prints one JSON line.
@@ -267,9 +269,14 @@ MAX_MARKS = 64
 
 
 def time_steps(tp, P, sets, phases, steps, warmup):
-    """Runs warmup + steps steps over the rotating sets.  Returns
-    (wall seconds of the timed steps, seconds per phase per step,
-     [(phase, kernel name, average seconds)] in launch order)."""
+    """Runs warmup steps, then `steps` timed steps with HIP events at the
+    phase boundaries only, then `steps` more with the library's per-kernel
+    marks armed (an event after every kernel).  The marks add a small gap
+    at each kernel boundary (an event record, a few microseconds), so the
+    phase times and the step time come from the first pass and the
+    per-kernel times from the second.  Returns (wall seconds of the first
+    pass, seconds per phase per step, [(phase, kernel name, average seconds)]
+    in launch order)."""
     import torch
     for i in range(warmup):
         for ph in phases:
@@ -278,30 +285,36 @@ def time_steps(tp, P, sets, phases, steps, warmup):
     mk = lambda: torch.cuda.Event(enable_timing=True)
     pev = [[mk() for _ in range(len(phases) + 1)] for _ in range(steps)]
     kev = [[mk() for _ in range(MAX_MARKS)] for _ in range(steps)]
+    k0 = [mk() for _ in range(steps)]
     # torch creates an event at its first record; do that now, outside the
     # timed region, so that the library can be handed the handles
-    for row in pev + kev:
-        for e in row:
-            e.record()
+    for e in sum(pev + kev, []) + k0:
+        e.record()
     torch.cuda.synchronize()
-    ph_marks = []        # per step: number of kernel marks at each phase boundary
-    names = None
     t0 = time.perf_counter()
     for i in range(steps):
         s = sets[i % len(sets)]
-        tp.tp_kernel_marks(kev[i])
-        bounds = [0]
         pev[i][0].record()
         for j, ph in enumerate(phases):
             run_phase(tp, P, s, ph)
             pev[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # second pass: per-kernel marks
+    ph_marks, names = [], None
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        tp.tp_kernel_marks(kev[i])
+        bounds = [0]
+        k0[i].record()
+        for ph in phases:
+            run_phase(tp, P, s, ph)
             bounds.append(tp.tp_kernel_marks_used())
         if names is None:
             names = tp.tp_kernel_mark_names()
         tp.tp_kernel_marks([])
         ph_marks.append(bounds)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ph_t = {p: 0.0 for p in phases}
     n_k = ph_marks[0][-1]
     if n_k >= MAX_MARKS:
@@ -311,7 +324,7 @@ def time_steps(tp, P, sets, phases, steps, warmup):
         for j, p in enumerate(phases):
             ph_t[p] += pev[i][j].elapsed_time(pev[i][j + 1]) * 1e-3
         for k in range(n_k):
-            prev = pev[i][0] if k == 0 else kev[i][k - 1]
+            prev = k0[i] if k == 0 else kev[i][k - 1]
             k_t[k] += prev.elapsed_time(kev[i][k]) * 1e-3
     ph_t = {p: v / steps for p, v in ph_t.items()}
     bounds = ph_marks[0]

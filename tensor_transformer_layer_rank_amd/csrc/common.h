@@ -158,6 +158,8 @@ struct GemmProblem {
   int64_t a_total;
   // EPI_SILU_BF16: rows from a gate row to its up row (0: li)
   int64_t up_off;
+  // m-tiles per group of the tile order (0: the kernel's default)
+  int group_m;
 };
 
 // Chooses a tile shape and launches.  When the grid would not fill the GPU

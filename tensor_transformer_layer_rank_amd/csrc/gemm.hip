@@ -125,10 +125,11 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   int tm, tn;
   {
     const int t = xcd_remap(blockIdx.x, gridDim.x);
-    const int per_group = GROUP_M * tiles_n;
+    const int group_m = p.group_m > 0 ? p.group_m : GROUP_M;
+    const int per_group = group_m * tiles_n;
     const int g = t / per_group;
-    const int first_m = g * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
     const int r = t - g * per_group;
     tm = first_m + r % gm;
     tn = r / gm;
@@ -576,10 +577,11 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   }
   auto coords = [&](int j, int64_t& m0, int64_t& nrow0) __attribute__((always_inline)) {
     const int t = first + j * step;
-    const int per_group = GROUP_M * tiles_n;
+    const int group_m = p.group_m > 0 ? p.group_m : GROUP_M;
+    const int per_group = group_m * tiles_n;
     const int gi = t / per_group;
-    const int first_m = gi * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int first_m = gi * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
     const int r = t - gi * per_group;
     m0 = (int64_t)(first_m + r % gm) * BM;
     nrow0 = (int64_t)(r / gm) * (EPI == EPI_SILU_BF16 ? BN / 2 : BN);
@@ -999,7 +1001,8 @@ double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int
   return (t_comp > t_mem ? t_comp : t_mem) + kLaunchUs + t_red;
 }
 
-Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool consumer_sums = false) {
+Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool consumer_sums = false,
+               double* cost_out = nullptr) {
   Plan best{V256x256, 1, K, 0, 0};
   double best_cost = 1e300;
   const int64_t kblocks = (K + 63) / 64;
@@ -1021,6 +1024,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
       }
     }
   }
+  if (cost_out) *cost_out = best_cost;
   return best;
 }
 
@@ -1135,25 +1139,38 @@ struct Schedule {
 };
 
 Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool gathered) {
-  Schedule sc{make_plan(M, N, K, epi, allow_split), 0, Plan{}};
-  const Plan& pl = sc.main;
-  if (pl.splits != 1 || gathered || !(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV)) return sc;
-  const Variant& v = kVariants[pl.v];
-  const int64_t R = (int64_t)kCUs * v.resident;
-  const int64_t T = (int64_t)pl.tiles_m * pl.tiles_n;
-  if (pl.v == V256x256 && epi == EPI_BF16 && T >= 8 * kCUs) return sc;   // persistent kernel
-  const int64_t full = T / R * R;
-  if (full == 0 || full == T || full % pl.tiles_m || (T - full) * 2 > R) return sc;
-  const int64_t bn_out = epi == EPI_SILU_BF16 ? v.bn / 2 : v.bn;
+  double best_cost = 0;
+  Schedule best{make_plan(M, N, K, epi, allow_split, false, &best_cost), 0, Plan{}};
+  if (gathered || !(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV)) return best;
   const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;
-  const int64_t c_split = full / pl.tiles_m * bn_out;
-  if (c_split >= ncols) return sc;
-  sc.c_split = c_split;
-  sc.main.tiles_n = (int)(full / pl.tiles_m);
-  const int64_t n2 = epi == EPI_SILU_BF16 ? 2 * (ncols - c_split) : ncols - c_split;
-  // a SiLU tail has its gate and up rows apart: it never splits K
-  sc.tail = make_plan(M, n2, K, epi, allow_split && epi != EPI_SILU_BF16);
-  return sc;
+  // each unsplit variant whose tiles leave a last round at most half full:
+  // its whole rounds, then the tail with the best plan for its own shape
+  for (int vi = 0; vi < V_COUNT; ++vi) {
+    const Variant& v = kVariants[vi];
+    if (epi == EPI_SILU_BF16 && !v.silu) continue;
+    if (epi == EPI_QKV && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
+    int64_t tm, tn;
+    plan_cost(v, M, N, K, epi, 1, &tm, &tn);
+    const int64_t R = (int64_t)kCUs * v.resident, T = tm * tn;
+    if (vi == V256x256 && epi == EPI_BF16 && T >= 8 * kCUs) continue;   // the persistent kernel's case
+    const int64_t full = T / R * R;
+    if (full == 0 || full == T || full % tm || (T - full) * 2 > R) continue;
+    const int64_t bn_out = epi == EPI_SILU_BF16 ? v.bn / 2 : v.bn;
+    const int64_t c_split = full / tm * bn_out;
+    if (c_split >= ncols) continue;
+    const int64_t n1 = epi == EPI_SILU_BF16 ? 2 * c_split : c_split;
+    const int64_t n2 = epi == EPI_SILU_BF16 ? 2 * (ncols - c_split) : ncols - c_split;
+    int64_t tm1, tn1;
+    const double c1 = plan_cost(v, M, n1, K, epi, 1, &tm1, &tn1);
+    double c2 = 0;
+    // a SiLU tail has its gate and up rows apart: it never splits K
+    const Plan tail = make_plan(M, n2, K, epi, allow_split && epi != EPI_SILU_BF16, false, &c2);
+    if (c1 + c2 < best_cost * 0.999) {
+      best_cost = c1 + c2;
+      best = Schedule{Plan{vi, 1, K, (int)tm1, (int)tn1}, c_split, tail};
+    }
+  }
+  return best;
 }
 
 // output columns [c0, c1) of p as a problem of its own
