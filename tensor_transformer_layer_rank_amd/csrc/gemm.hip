@@ -83,8 +83,9 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
   store_head_lanes(dst, x, j);
 }
 // the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
+// (the epilogue stages the tile 128 columns -- one head -- at a time)
 constexpr bool qkv_tile_ok(int bm, int bn, int stages, int bk = 64) {
-  return bn % 128 == 0 && bm * bn * 4 <= stages * (bm + bn) * bk * 2;
+  return bn % 128 == 0 && bm * 128 * 4 <= stages * (bm + bn) * bk * 2;
 }
 
 // Default LDS stages per tile shape: as many as let two workgroups share a
@@ -412,34 +413,39 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   }
   if constexpr (EPI == EPI_QKV) {
     static_assert(qkv_tile_ok(BM, BN, S, BK), "QKV tile must cover whole heads and fit the ring");
-    // stage the fp32 tile [BM][BN] in LDS (16-byte chunk c of row r at
-    // c ^ ((r >> 2) & 1): the two half-waves write rows 4 apart), then
-    // finish it 16 lanes per (row, head)
-    __syncthreads();
+    // one head (128 columns) at a time: stage its fp32 columns [BM][128] in
+    // LDS (16-byte chunk c of row r at c ^ ((r >> 2) & 1): the two
+    // half-waves write rows 4 apart), then finish it 16 lanes per row
     float* st = reinterpret_cast<float*>(smem);
-    auto st_off = [&](int r, int c) -> int { return r * BN + ((((c >> 2) ^ (r >> 2)) & 1) | ((c >> 2) & ~1)) * 4 + (c & 3); };
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          st[st_off(wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), ncol(j) + lr)] = acc[i][j][e];
-    __syncthreads();
+    auto st_off = [&](int r, int c) -> int { return r * 128 + ((((c >> 2) ^ (r >> 2)) & 1) | ((c >> 2) & ~1)) * 4 + (c & 3); };
     const int j16 = tid & 15;
     const RopeCoef rc = rope_coef(p.qkv.theta, j16);
     constexpr int HPT = BN / 128;                      // heads per tile
     const int heads = (int)(p.N / 128);
-    for (int u = tid >> 4; u < BM * HPT; u += NT / 16) {
-      const int r = u % BM, hh = u / BM;
-      const int64_t m = m0 + r;
+#pragma unroll
+    for (int hh = 0; hh < HPT; ++hh) {
+      __syncthreads();   // the ring (first head) or the previous head's staging is no longer read
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int c0 = ncol(j);
+        if (c0 / 128 != hh) continue;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            st[st_off(wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), c0 - hh * 128 + lr)] = acc[i][j][e];
+      }
+      __syncthreads();
       const int h = tn * HPT + hh;
-      if (m >= M || h >= heads) continue;
-      // four consecutive columns are one 16-byte group of the staged tile
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + st_off(r, hh * 128 + 4 * j16));
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + st_off(r, hh * 128 + 64 + 4 * j16));
-      float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      qkv_finish(p.qkv, x, m, h, j16, rc);
+      for (int r = tid >> 4; r < BM; r += NT / 16) {
+        const int64_t m = m0 + r;
+        if (m >= M || h >= heads) continue;
+        // four consecutive columns are one 16-byte group of the staged tile
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + st_off(r, 4 * j16));
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + st_off(r, 64 + 4 * j16));
+        float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        qkv_finish(p.qkv, x, m, h, j16, rc);
+      }
     }
     return;
   }
