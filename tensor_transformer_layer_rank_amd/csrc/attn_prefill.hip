@@ -393,14 +393,16 @@ bool attn_prefill_fills(int B, int T, int lq, int lkv) {
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
   const PrefillPlan p = prefill_plan(a.B, a.T, a.lq, a.lkv);
-  switch (a.lq / a.lkv) {
-    case 1: return launch<1, 1>(a, p, s);
-    case 2: return launch<2, 1>(a, p, s);
-    case 4: return launch<2, 2>(a, p, s);
-    case 8: return launch<2, 4>(a, p, s);
-    case 16: return launch<2, 4>(a, p, s);
-    default: return hipErrorInvalidValue;
-  }
+  // the kernel's wave shape comes from the same choice as the plan, and
+  // together they must cover the GQA group exactly
+  int hw, hg;
+  prefill_shape(a.lq / a.lkv, &hw, &hg);
+  if (a.lkv <= 0 || a.lq % a.lkv || hw * hg * p.hgroups != a.lq / a.lkv) return hipErrorInvalidValue;
+  if (hw == 1 && hg == 1) return launch<1, 1>(a, p, s);
+  if (hw == 2 && hg == 1) return launch<2, 1>(a, p, s);
+  if (hw == 2 && hg == 2) return launch<2, 2>(a, p, s);
+  if (hw == 2 && hg == 4) return launch<2, 4>(a, p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tps
