@@ -41,6 +41,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -342,6 +343,12 @@ def find_kernel(kernels, phase, pred):
     return None, None
 
 
+def gemm_dims(name):
+    """(M, N, K) of a GEMM-family mark name, e.g. gemm_tile<256,256,2>/silu[4096x24576x5120]."""
+    m = re.search(r"\[(\d+)x(\d+)x(\d+)\]$", name)
+    return tuple(int(v) for v in m.groups())
+
+
 def kernel_table(kernels):
     out, seen = {}, {}
     for p, name, t in kernels:
@@ -395,12 +402,16 @@ def run_bench(args):
     dec_gbps = dec_bytes / ph["decode"] / 1e9
 
     # dominant kernel: the prefill gate_up GEMM with its SiLU epilogue
-    gu_name, gu_t = find_kernel(kernels, "prefill", lambda s: s.endswith("/silu") and s.startswith("gemm_tile"))
-    gu_flops = fp["gate_up"]
-    gu_bytes = 2 * (T * H + 2 * L.li * H + T * L.li)
+    # (the first SiLU launch: with a tail schedule it covers the leading
+    # columns only, so its work is read from the launched M x N x K)
+    gu_name, gu_t = find_kernel(kernels, "prefill", lambda s: "/silu[" in s and s.startswith("gemm_tile"))
+    gm, gn, gk = gemm_dims(gu_name) if gu_name else (T, 2 * L.li, H)
+    gu_flops = 2 * gm * gn * gk
+    gu_bytes = 2 * (gm * gk + gn * gk + gm * gn // 2)
     gu_traffic = traffic_from_profile(f"gate_up_gemm_{args.workload}_hbm_traffic.txt", "gemm.hip")
     gu_tflops = gu_flops / gu_t / 1e12 if gu_t else None
-    roofline = {"kernel": f"{gu_name} (tp_mlp gate_up + SiLU*up, prefill {T} x {2 * L.li} x {H})",
+    roofline = {"kernel": f"{gu_name} (tp_mlp gate_up + SiLU*up of prefill {T} x {2 * L.li} x {H}: "
+                          f"the launch over output columns [0, {gn // 2}) of {L.li})",
                 "bound": "mfma", "achieved": round(gu_tflops, 1) if gu_tflops else None,
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tflops / MFMA_BF16_PEAK_TFLOPS, 4) if gu_tflops else None,

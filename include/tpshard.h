@@ -151,8 +151,10 @@ int tp_kernel_marks(void* const* events, int32_t n_events);
 int32_t tp_kernel_marks_used(void);
 
 /* Name of the kernel launched just before mark i on this thread, e.g.
- * "gemm_tile<256,256,2>/silu" or "attn_flash/decode"; "" when i is out of
- * range.  Valid until the next tp_kernel_marks call on this thread. */
+ * "gemm_tile<256,256,2>/silu[4096x24576x5120]" (GEMM family: tile, stages,
+ * epilogue and the launched M x N x K, N counting the rows of B) or
+ * "attn_flash/decode"; "" when i is out of range.  Valid until the next
+ * tp_kernel_marks call on this thread. */
 const char* tp_kernel_mark_name(int32_t i);
 
 /* ------------------------------------------------------------------------

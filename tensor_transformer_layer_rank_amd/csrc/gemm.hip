@@ -1034,12 +1034,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
   return best;
 }
 
-// timing mark after a GEMM-family launch: kernel, tile and epilogue
+// timing mark after a GEMM-family launch: kernel, tile, epilogue and the
+// launched product M x N x K (N = rows of B, so the launch does 2 M N K flops)
 const char* const kEpiNames[] = {"bf16", "f32", "silu", "qkv", "argmax"};
-void mark_gemm(hipStream_t s, const char* kern, int bm, int bn, int stages, int epi) {
+void mark_gemm(hipStream_t s, const char* kern, int bm, int bn, int stages, int epi, const GemmProblem& p) {
   if (!kmarks_armed()) return;
-  char buf[96];
-  snprintf(buf, sizeof buf, "%s<%d,%d,%d>/%s", kern, bm, bn, stages, kEpiNames[epi]);
+  char buf[128];
+  snprintf(buf, sizeof buf, "%s<%d,%d,%d>/%s[%lldx%lldx%lld]", kern, bm, bn, stages, kEpiNames[epi],
+           (long long)p.M, (long long)p.N, (long long)p.K);
   kmark(s, buf);
 }
 
@@ -1056,7 +1058,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     q.ldc = p.N;
     dim3 grid(pl.tiles_m * pl.tiles_n, pl.splits);
     gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
-    mark_gemm(s, "gemm_splitk", BM, BN, S, epi);
+    mark_gemm(s, "gemm_splitk", BM, BN, S, epi, p);
     if (!finish) return hipGetLastError();
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
     int64_t g = (p.M * (cols / 4) + 255) / 256;
@@ -1078,14 +1080,14 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   if constexpr ((BN / WGN / 32) % 2 == 0) {
     if (epi == EPI_SILU_BF16) {
       gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
-      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_SILU_BF16);
+      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_SILU_BF16, p);
       return hipGetLastError();
     }
   }
   if constexpr (qkv_tile_ok(BM, BN, S)) {
     if (epi == EPI_QKV) {
       gemm_kernel<BM, BN, WGM, WGN, EPI_QKV, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
-      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_QKV);
+      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_QKV, p);
       return hipGetLastError();
     }
   }
@@ -1093,14 +1095,14 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
     gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
-    mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX);
+    mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX, p);
     return hipGetLastError();
   }
   if (epi == EPI_BF16)
     gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   else
     gemm_kernel<BM, BN, WGM, WGN, EPI_F32, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
-  mark_gemm(s, "gemm_tile", BM, BN, S, epi);
+  mark_gemm(s, "gemm_tile", BM, BN, S, epi, p);
   return hipGetLastError();
 }
 
@@ -1144,10 +1146,22 @@ struct Schedule {
   Plan tail;
 };
 
+// eight or more rounds of 256 x 256 tiles with a bf16 output: one persistent
+// workgroup per CU (measured: faster from about that many rounds on, when the
+// per-tile fill and relaunch it saves are a visible part of a tile's time)
+bool persistent_plan(const Plan& pl, int epi, bool gathered) {
+  return pl.v == V256x256 && pl.splits == 1 && epi == EPI_BF16 && !gathered &&
+         (int64_t)pl.tiles_m * pl.tiles_n >= 8 * kCUs;
+}
+
 Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool gathered) {
   double best_cost = 0;
   Schedule best{make_plan(M, N, K, epi, allow_split, false, &best_cost), 0, Plan{}};
   if (gathered || !(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV)) return best;
+  // the persistent kernel spreads a ragged last round over its walk; on the
+  // lm_head shapes it measured faster than every tail schedule, which the
+  // per-tile cost model does not see
+  if (persistent_plan(best.main, epi, false)) return best;
   const int64_t ncols = epi == EPI_SILU_BF16 ? N / 2 : N;
   // each unsplit variant whose tiles leave a last round at most half full:
   // its whole rounds, then the tail with the best plan for its own shape
@@ -1248,12 +1262,9 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
                          scratch_bytes >= gemm_scratch_bytes(p.M, p.N, p.K, epi);
   const Schedule sc = make_schedule(p.M, p.N, p.K, epi, can_split, p.a_rows != nullptr);
   const Plan& pl = sc.main;
-  // eight or more rounds of 256 x 256 tiles: one persistent workgroup per
-  // CU (measured: faster from about that many rounds on, when the per-tile
-  // fill and relaunch it saves are a visible part of a tile's time)
-  if (pl.v == V256x256 && pl.splits == 1 && epi == EPI_BF16 && !p.a_rows && (int64_t)pl.tiles_m * pl.tiles_n >= 8 * kCUs) {
+  if (persistent_plan(pl, epi, p.a_rows != nullptr)) {
     gemm_persist_kernel<256, 256, 4, 2, EPI_BF16, 8, 2><<<kCUs, 512, 0, s>>>(p, pl.tiles_m, pl.tiles_n);
-    mark_gemm(s, "gemm_persist", 256, 256, 2, EPI_BF16);
+    mark_gemm(s, "gemm_persist", 256, 256, 2, EPI_BF16, p);
     return hipGetLastError();
   }
   if (!sc.c_split) return launch_plan(p, epi, pl, scratch, s);
