@@ -3,10 +3,11 @@
 // T new tokens after `past` cached ones; query t (position past + t) sees
 // keys 0 .. past + t, q head i reads kv head i / rep, scale 1/sqrt(128).
 //
-// Flash attention on MFMA (v_mfma_f32_32x32x16_bf16).  A workgroup is four
-// waves working on one kv head:
-//  * each wave owns 32 query rows of HW q heads of that kv head (HW = 2 under
-//    GQA, else 1), so every K or V operand it reads from LDS feeds HW MFMAs;
+// Flash attention on MFMA (v_mfma_f32_32x32x16_bf16).  A workgroup is eight
+// waves, two per SIMD, working on one kv head:
+//  * each wave owns 32 query rows of HW q heads of that kv head (HW = 1: with
+//    two waves per SIMD the registers allow one head, and the other wave's
+//    MFMAs run while a wave does its softmax on the VALU);
 //  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads
 //    with the lds flag) through a ring of NS stages; 16-byte chunks of a key
 //    row are XOR-swizzled by a rotation of the key so that operand reads avoid bank
@@ -20,8 +21,8 @@
 //  * the softmax runs in the exp2 domain with a running max per query.
 // Early query blocks need few keys; heavy (late) blocks are launched first.
 // This kernel serves prefills whose blocks alone fill the GPU; smaller ones
-// go to the one-pass kernel of attn_flash.hip, which splits each block's
-// keys among its waves instead.
+// (and GQA ratios it has no wave shape for) go to the one-pass kernel of
+// attn_flash.hip, which splits each block's keys among its waves instead.
 #include <type_traits>
 
 #include "common.h"
@@ -35,7 +36,6 @@ typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 constexpr int kKeys = 64;                    // keys per tile
 constexpr int kTile = kKeys * 256;           // bytes of one K or V tile (64 rows x 128 bf16)
 constexpr int kStage = 2 * kTile;            // K tile, then V tile
-constexpr int kLoadsPerWave = kStage / 1024 / 4;
 constexpr float kQScale = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
 constexpr float kSlack = 8.f;                 // lazy-rescale margin, log2 units
 
@@ -89,10 +89,13 @@ __host__ __device__ inline int rb_tiles(int T, int past, int rows, int r) {
   const int end = (r + 1) * rows < T ? (r + 1) * rows : T;
   return (past + end + kKeys - 1) / kKeys;
 }
-template <int HW, int HG, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NWV waves (NWV / 4 per SIMD), HG of them along the heads; NS ring stages
+template <int HW, int HG, int NS, int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
-  constexpr int RB = 4 / HG;           // 32-row blocks per workgroup
+  static_assert(NWV % HG == 0 && (kStage / 1024) % (2 * NWV) == 0, "waves split the rows and the tile loads");
+  constexpr int kLoadsPerWave = kStage / 1024 / NWV;
+  constexpr int RB = NWV / HG;         // 32-row blocks per workgroup
   constexpr int WGH = HW * HG;         // q heads per workgroup
   // one array per ring stage: reads of one stage then carry alias scopes
   // that tell them apart from direct-to-LDS loads still landing in another,
@@ -154,8 +157,8 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
   auto dma_tile = [&](int kt, auto st) {
     const uint32_t base = lds_addr(stage(st));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = wave * 4 + j;
+    for (int j = 0; j < kLoadsPerWave / 2; ++j) {
+      const int i = wave * (kLoadsPerWave / 2) + j;
       const int key = 4 * i + (lane >> 4);
       const uint32_t off = (uint32_t)(kt * kKeys + key) * 256u + (uint32_t)(((lane & 15) ^ kswz(key)) << 4);
       dma16(rk, off, base + i * 1024);
@@ -203,24 +206,6 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
       }
     const int key0 = kt * kKeys;
     const bool diag = key0 + kKeys - 1 > a.past + t0w;     // some key may follow some row
-    // V^T operands do not depend on P: their transposing reads go out first
-    // and land while the VALU does the softmax
-    bf16x8 vf[4][2][2];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const int key = kb * 32 + sub * 16 + tr_key;
-          const int d = db * 32 + tr_d;
-          const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
-          const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
-          const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
-          const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
-          vf[db][kb][sub] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        }
-    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[HW][4];
 #pragma unroll
     for (int hw = 0; hw < HW; ++hw) {
@@ -266,6 +251,22 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
         }
       l_run[hw] += ps;
     }
+    // V^T operands (another wave's work covers their latency)
+    bf16x8 vf[4][2][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int key = kb * 32 + sub * 16 + tr_key;
+          const int d = db * 32 + tr_d;
+          const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
+          const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+          const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
+          const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
+          vf[db][kb][sub] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -355,20 +356,23 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
   }
 }
 
-constexpr int kStages = 3;
-
-// q heads per wave and waves along the heads for a GQA ratio
-void prefill_shape(int rep, int* hw, int* hg) {
-  *hw = rep >= 2 ? 2 : 1;
-  const int g = rep / *hw;
-  *hg = g < 4 ? g : 4;
+// Two ring stages: with two waves per SIMD a third measured no faster, and
+// it costs registers.
+constexpr int kStages = 2;
+constexpr int kWaves = 8;
+// q heads per wave and waves along the heads for a GQA ratio; false when no
+// kernel instance has that shape
+bool prefill_shape(int rep, int* hw, int* hg) {
+  *hw = 1;
+  *hg = rep < kWaves ? rep : kWaves;
+  return rep >= 1 && (*hg == 1 || *hg == 2 || *hg == 4 || *hg == 8) && rep % *hg == 0;
 }
 
 PrefillPlan prefill_plan(int B, int T, int lq, int lkv) {
   int hw, hg;
-  prefill_shape(lq / lkv, &hw, &hg);
+  (void)prefill_shape(lq / lkv, &hw, &hg);
   PrefillPlan p{};
-  p.rows = 32 * (4 / hg);
+  p.rows = 32 * (kWaves / hg);
   p.n_rb = (T + p.rows - 1) / p.rows;
   p.hgroups = lq / lkv / (hw * hg);
   return p;
@@ -377,7 +381,7 @@ PrefillPlan prefill_plan(int B, int T, int lq, int lkv) {
 template <int HW, int HG>
 hipError_t launch(const AttnArgs& a, const PrefillPlan& p, hipStream_t s) {
   const int64_t groups = (int64_t)a.B * a.lkv * p.hgroups;
-  attn_prefill_kernel<HW, HG, kStages><<<(unsigned)(groups * p.n_rb), 256, 0, s>>>(a, p);
+  attn_prefill_kernel<HW, HG, kStages, kWaves><<<(unsigned)(groups * p.n_rb), kWaves * 64, 0, s>>>(a, p);
   kmark(s, "attn_prefill");
   return hipGetLastError();
 }
@@ -385,23 +389,25 @@ hipError_t launch(const AttnArgs& a, const PrefillPlan& p, hipStream_t s) {
 }  // namespace
 
 bool attn_prefill_fills(int B, int T, int lq, int lkv) {
-  if (B <= 0 || T <= 0 || lkv <= 0) return false;
+  if (B <= 0 || T <= 0 || lkv <= 0 || lq % lkv) return false;
+  int hw, hg;
+  if (!prefill_shape(lq / lkv, &hw, &hg)) return false;
   const PrefillPlan p = prefill_plan(B, T, lq, lkv);
   return (int64_t)B * lkv * p.hgroups * p.n_rb >= 256;
 }
 
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
-  const PrefillPlan p = prefill_plan(a.B, a.T, a.lq, a.lkv);
   // the kernel's wave shape comes from the same choice as the plan, and
   // together they must cover the GQA group exactly
   int hw, hg;
-  prefill_shape(a.lq / a.lkv, &hw, &hg);
-  if (a.lkv <= 0 || a.lq % a.lkv || hw * hg * p.hgroups != a.lq / a.lkv) return hipErrorInvalidValue;
+  if (a.lkv <= 0 || a.lq % a.lkv || !prefill_shape(a.lq / a.lkv, &hw, &hg)) return hipErrorInvalidValue;
+  const PrefillPlan p = prefill_plan(a.B, a.T, a.lq, a.lkv);
+  if (hw * hg * p.hgroups != a.lq / a.lkv) return hipErrorInvalidValue;
   if (hw == 1 && hg == 1) return launch<1, 1>(a, p, s);
-  if (hw == 2 && hg == 1) return launch<2, 1>(a, p, s);
-  if (hw == 2 && hg == 2) return launch<2, 2>(a, p, s);
-  if (hw == 2 && hg == 4) return launch<2, 4>(a, p, s);
+  if (hw == 1 && hg == 2) return launch<1, 2>(a, p, s);
+  if (hw == 1 && hg == 4) return launch<1, 4>(a, p, s);
+  if (hw == 1 && hg == 8) return launch<1, 8>(a, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -55,6 +55,7 @@ MID = {
     "rep8": dict(hidden=512, intermediate=1024, n_q_heads=16, n_kv_heads=2, head_dim=128, vocab=777, tp=2),
     "rep1": dict(hidden=264, intermediate=528, n_q_heads=4, n_kv_heads=4, head_dim=128, vocab=64, tp=2),
     "rep16": dict(hidden=384, intermediate=768, n_q_heads=32, n_kv_heads=2, head_dim=128, vocab=100, tp=2),
+    "rep4": dict(hidden=320, intermediate=640, n_q_heads=16, n_kv_heads=4, head_dim=128, vocab=200, tp=2),
 }
 MID_WID = {k: 100 + i for i, k in enumerate(MID)}
 
@@ -463,20 +464,21 @@ def test_qkv_attn_mid(name, phase):
         check_attn(w, wid, r, B, T, past, S_max, Wg=Wg, W=W)
 
 
-@pytest.mark.parametrize("name", ["rep1", "rep2", "rep4-replicated", "rep8", "rep16"])
+@pytest.mark.parametrize("name", ["rep1", "rep2", "rep4-replicated", "rep4", "rep8", "rep16"])
 @pytest.mark.parametrize("past", [0, 37])
 def test_qkv_attn_gqa_prefill_kernel(name, past):
     """Prefills wide enough that the GQA-sharing prefill kernel runs (its
     (kv head, row block) workgroups alone fill the GPU), at every group size
-    (rep 1, 2, 4 with a replicated kv head, 8, 16), from an empty cache and
+    (local rep 1, 2, 2 with a replicated kv head, 4, 8, 16), from an empty cache and
     after 37 cached positions (the causal offset of its row blocks).  The
     kernel marks confirm which attention kernel ran."""
     w, wid = MID[name], MID_WID[name]
     W = synth.full_weights(wid, w)
     Wg = {k: v.to(DEV) for k, v in W.items()}
     # (kv head, row block) workgroups: B * lkv * head groups * ceil(T / rows)
-    # >= 256 with 333 tokens (128-row blocks for rep 1 and 2, 32 for 8 and 16)
-    B = {"rep1": 48, "rep2": 48, "rep4-replicated": 96, "rep8": 24, "rep16": 24}[name]
+    # >= 256 with 333 tokens (rows = 32 * 8 / min(rep, 8): 256-row blocks for
+    # rep 1, 128 for rep 2, 64 for rep 4, 32 for 8 and 16)
+    B = {"rep1": 64, "rep2": 48, "rep4-replicated": 96, "rep4": 24, "rep8": 24, "rep16": 24}[name]
     T = 333
     S_max = past + T + 3
     rows = np.unique(np.concatenate([[0, 31, 32, T - 1, T, B * T - 1],
