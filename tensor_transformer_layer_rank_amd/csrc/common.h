@@ -160,6 +160,9 @@ struct GemmProblem {
   int64_t up_off;
   // m-tiles per group of the tile order (0: the kernel's default)
   int group_m;
+  // EPI_ARGMAX: id of this problem's column 0 (a column slice of a wider
+  // problem reports ids of the whole one)
+  int64_t col0;
 };
 
 // Chooses a tile shape and launches.  When the grid would not fill the GPU

@@ -384,9 +384,9 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
         for (int j = 0; j < TN; ++j) {
           const int64_t col = (int64_t)tn * BN + ncol(j) + lr;
           const float v = bf2f(f2bf(acc[i][j][e]));
-          if (col < p.N && better(v, (int)col, bv, bi)) {
+          if (col < p.N && better(v, (int)(p.col0 + col), bv, bi)) {
             bv = v;
-            bi = (int)col;
+            bi = (int)(p.col0 + col);
           }
         }
         cand_best32(bv, bi);
@@ -993,13 +993,22 @@ double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int
   const double t_comp = rounds * (kb * v.t_kb_us + out_kb * kEpiUsPerKB);
   const double partial = splits > 1 ? (double)splits * M * N * 4 : 0.0;
   const double bytes = (double)N * K * 2 + (double)M * K * 2 + partial;
-  const double active = (double)(wgs < resident ? wgs : resident);
-  const double rate = active * kWgBytesPerUs < kHbmBytesPerUs ? active * kWgBytesPerUs : kHbmBytesPerUs;
-  // Idle CUs are charged through the rate: a grid with fewer workgroups
-  // than it takes to saturate HBM streams at their summed per-workgroup
-  // rate.  (Sweeps of every plan on the decode shapes of the 0.6B and 32B
-  // shards put the chosen plan within about 1 us of the measured best.)
-  const double t_mem = bytes / rate;
+  // Idle CUs are charged through the rate: a round with fewer workgroups
+  // than it takes to saturate HBM streams its share of the bytes at their
+  // summed per-workgroup rate.  That is a grid below one round, and for a
+  // tile that fits once per CU also the ragged last round of a longer grid;
+  // with two per CU the leftover workgroups start beside running ones or
+  // alone on a CU, and measured no such loss.  (Sweeps of every plan on the
+  // decode shapes of the 0.6B and 32B shards put the chosen plan within
+  // about 1 us of the measured best.)
+  auto round_us = [&](int64_t active) {
+    const double rate = active * kWgBytesPerUs < kHbmBytesPerUs ? active * kWgBytesPerUs : kHbmBytesPerUs;
+    return (double)active * (bytes / (double)wgs) / rate;
+  };
+  const int64_t full_rounds = v.resident == 1 ? wgs / resident : 0;
+  const int64_t last = v.resident == 1 ? wgs % resident : (wgs < resident ? wgs : resident);
+  const double t_mem = v.resident == 1 ? (double)full_rounds * round_us(resident) + (last ? round_us(last) : 0.0)
+                                       : (double)wgs / (double)last * round_us(last);
   // the reduction runs after the GEMM: it reads every partial and writes C
   const double t_red = splits <= 1 ? 0.0
                       : consumer_sums ? partial / kHbmBytesPerUs
@@ -1157,7 +1166,12 @@ bool persistent_plan(const Plan& pl, int epi, bool gathered) {
 Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool gathered) {
   double best_cost = 0;
   Schedule best{make_plan(M, N, K, epi, allow_split, false, &best_cost), 0, Plan{}};
-  if (gathered || !(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV)) return best;
+  if (!(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV || epi == EPI_ARGMAX)) return best;
+  // a row gather reads A the same way in every column slice; the schedule of
+  // a gathered problem is the plain one for the argmax epilogue (whose
+  // candidate count the host sizes from the plain schedule) and has no tail
+  // otherwise
+  if (gathered && epi != EPI_ARGMAX) return best;
   // the persistent kernel spreads a ragged last round over its walk; on the
   // lm_head shapes it measured faster than every tail schedule, which the
   // per-tile cost model does not see
@@ -1205,6 +1219,9 @@ GemmProblem col_slice(const GemmProblem& p, int epi, int64_t c0, int64_t c1) {
   } else if (epi == EPI_QKV) {
     q.N = c1 - c0;
     q.qkv.head0 = p.qkv.head0 + (int)(c0 / 128);
+  } else if (epi == EPI_ARGMAX) {
+    q.N = c1 - c0;       // the caller moves C to the slice's first candidate
+    q.col0 = p.col0 + c0;
   } else {
     q.N = c1 - c0;
     q.C = static_cast<bf16*>(p.C) + c0;
@@ -1235,7 +1252,8 @@ size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K, int epi) {
 
 int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0) return 0;
-  return make_plan(M, N, K, EPI_ARGMAX, false).tiles_n;
+  const Schedule sc = make_schedule(M, N, K, EPI_ARGMAX, false, false);
+  return sc.main.tiles_n + (sc.c_split ? sc.tail.tiles_n : 0);
 }
 
 namespace {
@@ -1271,7 +1289,11 @@ hipError_t gemm_bf16(const GemmProblem& p, int epi, void* scratch, size_t scratc
   const int64_t ncols = epi == EPI_SILU_BF16 ? p.li : p.N;
   const hipError_t e = launch_plan(col_slice(p, epi, 0, sc.c_split), epi, pl, scratch, s);
   if (e != hipSuccess) return e;
-  return launch_plan(col_slice(p, epi, sc.c_split, ncols), epi, sc.tail, scratch, s);
+  GemmProblem tail = col_slice(p, epi, sc.c_split, ncols);
+  // argmax: the tail's candidates follow the main launch's N tiles in each
+  // row (ldc counts both)
+  if (epi == EPI_ARGMAX) tail.C = static_cast<uint64_t*>(p.C) + pl.tiles_n;
+  return launch_plan(tail, epi, sc.tail, scratch, s);
 }
 
 hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, bool defer, int* splits_out,
