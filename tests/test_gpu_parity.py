@@ -690,6 +690,36 @@ def test_lm_head_argmax_full_size_sampled(wid):
     check(gv, gi, rv, ri)
 
 
+@pytest.mark.parametrize("M", [128, 256, 100, 64])
+def test_lm_head_argmax_matches_logits_argmax(M):
+    """Every row of the 32B tp=2 decode head (hidden 5120, rank 1's 75968-row
+    vocab slice): the argmax-epilogue GEMM, whose schedule may split the
+    columns into a main launch and a tail (128 and 256 rows here), returns
+    for each row exactly the first maximum of the logits that tp_lm_head
+    computes on the GPU (no split-K in either, so both round the same fp32
+    sums), with ids from the whole slice."""
+    w = synth.WORKLOADS[4]
+    V, H, n = w["vocab"], w["hidden"], w["tp"]
+    c = tp.Cfg(hidden=H, vocab=V, tp_size=n, tp_rank=1)
+    L = tp.tp_local_dims(c)
+    nv = L.vocab_end - L.vocab_start
+    E = _big_vocab(V, H)
+    x = synth.activations(40 + M, M, H).to(DEV)
+    shard = torch.empty(nv, H, dtype=torch.bfloat16, device=DEV)
+    tp.tp_shard_weights(c, tp.TP_W_VOCAB, E.to(DEV), shard)
+    ws = torch.empty(tp.tp_workspace_bytes(c, tp.TP_OP_LM_ARGMAX, M, 1), dtype=torch.uint8, device=DEV)
+    v = torch.empty(M, dtype=torch.float32, device=DEV)
+    i = torch.empty(M, dtype=torch.int32, device=DEV)
+    tp.tp_lm_head_argmax(c, x, M, shard, v, i, ws)
+    lg = torch.empty(M, nv, dtype=torch.bfloat16, device=DEV)
+    tp.tp_lm_head(c, x, M, shard, lg)
+    torch.cuda.synchronize()
+    lgf = lg.float().cpu().numpy()
+    ref_i = np.argmax(lgf, axis=1)
+    assert np.array_equal(i.cpu().numpy(), ref_i + L.vocab_start)
+    assert np.array_equal(v.cpu().numpy(), lgf[np.arange(M), ref_i])
+
+
 @pytest.mark.parametrize("case", ["ragged-ties", "empty-shard", "resident-ties", "resident-empty-shard",
                                   "resident-one-row", "resident-h256", "resident-m20", "resident-h768"])
 def test_lm_head_argmax_ragged(case):
