@@ -469,17 +469,31 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   // chunks XOR-swizzled by row), then writes whole 16-byte row chunks.
   constexpr int OC = EPI == EPI_SILU_BF16 ? WN / 2 : WN;     // output columns per wave
   constexpr int OCH = OC / 8;                                // 16-byte chunks per staged row
-  static_assert(WM * OC * 2 * WGM * WGN <= S * STAGE * 2, "staging does not fit");
-  bf16* so = smem + wave * (WM * OC);
+  // rows staged per pass: the whole wave tile, or 32 rows at a time where
+  // that does not fit the ring (256 x 320 tiles)
+  constexpr int PR = WM * OC * 2 * WGM * WGN <= S * STAGE * 2 ? WM : 32;
+  static_assert(PR * OC * 2 * WGM * WGN <= S * STAGE * 2, "staging does not fit");
+  bf16* so = smem + wave * (PR * OC);
   // the staging area overlaps ring stages that slower waves may still be
   // reading for the last K block
   __syncthreads();
-  auto so_idx = [&](int r, int c) { return r * OC + (((c >> 3) ^ (r & (OCH - 1))) << 3) + (c & 7); };
+  // chunk c of staged row r sits at chunk och(r, c): XOR-swizzled by the
+  // row, or rotated by it where a row's chunk count is not a power of two
+  auto och = [&](int r, int c) { return (OCH & (OCH - 1)) == 0 ? c ^ (r & (OCH - 1)) : (c + r) % OCH; };
+  auto so_idx = [&](int r, int c) { return r * OC + (och(r, c >> 3) << 3) + (c & 7); };
+  const int64_t ncols = EPI == EPI_SILU_BF16 ? p.li : p.N;
+  const int64_t col0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) + wn * (WN / 2) : (int64_t)tn * BN + wn * WN;
+  bf16* C = static_cast<bf16*>(p.C);
+  const bool vec = (p.ldc % 8) == 0;
+  // A pass rewrites staging rows the previous pass read; one wave's LDS
+  // accesses run in order, so it needs no wait.
+#pragma unroll
+  for (int ps = 0; ps < WM / PR; ++ps) {
   // (C^T layout: row i * 32 + lr, columns j * 32 + 8 * g4 + 4 * lh .. + 3)
 #pragma unroll
   for (int j = 0; j < (EPI == EPI_SILU_BF16 ? TN / 2 : TN); ++j)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = ps * (PR / 32); i < (ps + 1) * (PR / 32); ++i)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         float v[4];
@@ -493,22 +507,18 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
             v[q] = acc[i][j][e];
           }
         }
-        *reinterpret_cast<u32x2*>(so + so_idx(i * 32 + lr, j * 32 + 8 * g4 + 4 * lh)) =
+        *reinterpret_cast<u32x2*>(so + so_idx(i * 32 - ps * PR + lr, j * 32 + 8 * g4 + 4 * lh)) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
   __builtin_amdgcn_wave_barrier();
-  const int64_t ncols = EPI == EPI_SILU_BF16 ? p.li : p.N;
-  const int64_t col0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) + wn * (WN / 2) : (int64_t)tn * BN + wn * WN;
-  const int64_t row0 = m0 + wm * WM;
-  bf16* C = static_cast<bf16*>(p.C);
-  const bool vec = (p.ldc % 8) == 0;
+  const int64_t row0 = m0 + wm * WM + ps * PR;
 #pragma unroll 4
-  for (int q = lane; q < WM * OCH; q += 64) {
+  for (int q = lane; q < PR * OCH; q += 64) {
     const int r = q / OCH, c = q % OCH;
     const int64_t gm = row0 + r, gc = col0 + c * 8;
     if (gm >= M || gc >= ncols) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * OC + ((c ^ (r & (OCH - 1))) << 3));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * OC + (och(r, c) << 3));
     if (vec && gc + 8 <= ncols) {
       // streaming store: the output is not read again by this kernel, and
       // allocating it in L2 would evict the A/B panels that other tiles
@@ -519,6 +529,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       for (int t = 0; t < 8; ++t)
         if (gc + t < ncols) C[gm * p.ldc + gc + t] = __builtin_bit_cast(bf16, (uint16_t)(v[t >> 1] >> (16 * (t & 1))));
     }
+  }
   }
 }
 
@@ -957,12 +968,22 @@ struct Variant {
   float t_kb_us;       // time per 64-wide K block per resident round at full load
   bool silu;           // wave tile has an even number of 32-column blocks
 };
-enum VariantId { V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V_COUNT };
+// V256x320: 256 x 320 tiles (waves of 64 x 160) for the row-parallel
+// projections, whose N = 5120 is 16 such tiles: at 4096 rows that is one
+// round of 256 tiles, where 256-wide tiles need 1.25 rounds (or a second
+// launch for the last 1024 columns).  Bf16 and fp32 outputs only (a
+// 320-wide tile holds neither whole 128-column heads nor gate/up pairs),
+// and only for single-round grids: longer grids keep the persistent kernel.
+enum VariantId {
+  V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V256x320, V_COUNT
+};
 constexpr Variant kVariants[V_COUNT] = {
     {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.59f, true},
     {128, 128, 2, 2, 1.08f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
-    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},
+    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.45f, false},
 };
+// the planner offers the 320-wide tile to plain outputs on one round only
+constexpr bool plain_out_only(int bn) { return bn == 320; }
 // Constants fitted to a sweep of every (variant, split) plan over the
 // decode, prefill, lm_head and decode-argmax shapes of the Qwen3-0.6B / 32B
 // shards on MI355X (27 shapes; the chosen plans are within 1% of the
@@ -1028,10 +1049,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
     for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
       if (sp > 1 && (!allow_split || !quad_cols || kblocks < 4 * sp)) break;
       if (epi == EPI_SILU_BF16 && !v.silu) continue;
+      if (plain_out_only(v.bn) && (epi == EPI_QKV || epi == EPI_ARGMAX)) continue;
       if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
       const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn, consumer_sums) * (sp > 1 ? 1.05 : 1.0);
+      if (plain_out_only(v.bn) && tm * tn * sp > kCUs) continue;
       if (c < best_cost * 0.999) {
         best_cost = c;
         const int64_t kps = sp == 1 ? K : ((kblocks + sp - 1) / sp) * 64;
@@ -1103,9 +1126,12 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   // the planner never picks a variant that cannot run the epilogue
   if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
-    gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
-    mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX, p);
-    return hipGetLastError();
+    if constexpr (!plain_out_only(BN)) {
+      gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
   }
   if (epi == EPI_BF16)
     gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
@@ -1182,6 +1208,7 @@ Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_spli
   for (int vi = 0; vi < V_COUNT; ++vi) {
     const Variant& v = kVariants[vi];
     if (epi == EPI_SILU_BF16 && !v.silu) continue;
+    if (plain_out_only(v.bn)) continue;   // a single-round tile: no whole rounds to split off
     if (epi == EPI_QKV && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
     int64_t tm, tn;
     plan_cost(v, M, N, K, epi, 1, &tm, &tn);
@@ -1268,6 +1295,7 @@ hipError_t launch_plan(const GemmProblem& p, int epi, const Plan& pl, void* scra
     case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, epi, pl, scratch, s, finish);
     case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s, finish);
     case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s, finish);
+    case V256x320: return launch_tile<256, 320, 4, 2, 2>(p, epi, pl, scratch, s, finish);
     default: return launch_tile<64, 64, 2, 2, 8>(p, epi, pl, scratch, s, finish);
   }
 }
@@ -1315,6 +1343,7 @@ hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, b
     case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, !split);
     case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, !split);
     case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
+    case V256x320: return hipErrorInvalidValue;   // never planned for QKV
     default: return launch_tile<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, !split);
   }
 }

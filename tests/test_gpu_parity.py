@@ -358,6 +358,33 @@ def test_mlp_full_size_sampled(wid):
         assert relerr(f64(part)[rows], p_ref) <= TOL_BF16, (wid, M, "partial")
 
 
+def test_mlp_wide_tile_ragged():
+    """The row-parallel down projection on its 320-column tiles, element by
+    element: hidden 4904 is 15 tiles and a 104-column tail, the 3900 rows 15
+    tiles and a 60-row tail (the last wave rows of a tile are written in a
+    second staging pass).  The kernel marks confirm the tile shape ran."""
+    w = dict(hidden=4904, intermediate=1280, n_q_heads=2, n_kv_heads=2, head_dim=128, vocab=0, tp=2)
+    wid, M = 120, 3900
+    W = synth.full_weights(wid, w)
+    rk = Rank(w, 1, {k: v.to(DEV) for k, v in W.items()})
+    oc = ocfg(w, 1)
+    gu = O.merge_gate_up(shard64(oc, O.W_GATE, W["gate"]), shard64(oc, O.W_UP, W["up"]))
+    down = shard64(oc, O.W_DOWN, W["down"])
+    x = synth.activations(wid, M, w["hidden"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    tp.tp_kernel_marks(ev)
+    try:
+        h, part = run_mlp(rk, x.to(DEV), M)
+        torch.cuda.synchronize()
+        names = tp.tp_kernel_mark_names()
+    finally:
+        tp.tp_kernel_marks([])
+    assert any(n.startswith("gemm_tile<256,320,2>/bf16[3900x4904x640]") for n in names), names
+    h_ref, p_ref = O.mlp(oc, synth.to_f64(x), gu, down)
+    assert relerr(f64(h), h_ref) <= TOL_BF16
+    assert relerr(f64(part), p_ref) <= TOL_BF16
+
+
 # ------------------------------------------------------------------ attention
 
 def make_cache(w, wid, rk, B, S_max, past, n_global_kv):
