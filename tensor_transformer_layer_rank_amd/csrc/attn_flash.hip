@@ -131,6 +131,36 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
   const int nt = (n_keys + kKeys - 1) / kKeys;
   const int w0 = wave * nt / NWV, w1 = (wave + 1) * nt / NWV;   // this wave's tiles
 
+  // K/V tile loads: load i (0..7) of a tile holds keys 4i .. 4i+3; lane l
+  // writes physical chunk l % 16 of key 4i + l / 16.  Keys at or past
+  // past + T read as zero (descriptor bound) and are masked.
+  const int64_t slab = ((int64_t)b * a.lkv + kvh) * a.S_max * 128;
+  const uint32_t valid_bytes = (uint32_t)(a.past + a.T) * 256u;
+  const i32x4 rk = buffer_rsrc(a.k_cache + slab, valid_bytes);
+  const i32x4 rv = buffer_rsrc(a.v_cache + slab, valid_bytes);
+  unsigned char* ring = smem + wave * kWaveRingB;
+  // a stage: K of tile kt and V of tile kt (PIPE: of tile kt - 1).  A tile
+  // outside the wave's range may be loaded and is never read; below key 0
+  // the offset wraps past the descriptor bound and reads zero.
+  auto dma_tile = [&](int kt, int st) {
+    const uint32_t base = lds_addr(ring + st * kStageB);
+    const int vt = PIPE ? kt - 1 : kt;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int key = 4 * i + (lane >> 4);
+      const uint32_t sw = (uint32_t)(((lane & 15) ^ kswz(key)) << 4);
+      dma16(rk, (uint32_t)(kt * kKeys + key) * 256u + sw, base + i * 1024);
+      dma16(rv, (uint32_t)(vt * kKeys + key) * 256u + sw, base + kTileB + i * 1024);
+    }
+  };
+
+  // Decode issues each wave's first K/V tile before Q is ready, so that its
+  // load latency overlaps the Q prologue.  With the projection deferred, the
+  // tile that holds position past is written by the prologue below: a wave
+  // whose first tile is that one waits for it instead.
+  const bool early = decode && w1 > w0 && (a.qkv_splits == 0 || w0 < nt - 1);
+  if (early) dma_tile(w0, 0);
+
   // Q^T operands: lane supplies q[row lr, ks*16 + lh*8 .. +8]
   bf16x8 qf[8];
   if (decode && a.qkv_splits > 0) {
@@ -141,7 +171,8 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
     const int n_qkv = (a.lq + 2 * a.lkv) * 128;
     const int64_t plane = (int64_t)a.B * n_qkv;
     const float* prow = a.qkv_part + (int64_t)b * n_qkv;
-    bf16* qs = reinterpret_cast<bf16*>(smem);          // [rep][128]
+    // [rep][128] in wave 0's second ring stage (the first may hold an early tile)
+    bf16* qs = reinterpret_cast<bf16*>(smem + kStageB);
     const int j16 = tid & 15;
     const RopeCoef rc = rope_coef(a.theta, j16);
     for (int u = tid >> 4; u < rep + 2; u += NT / 16) {   // a unit: 16 lanes, one head row
@@ -186,29 +217,6 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
     // the compiler wait for every load in flight there
     wait_vm<0>();
   }
-
-  // K/V tile loads: load i (0..7) of a tile holds keys 4i .. 4i+3; lane l
-  // writes physical chunk l % 16 of key 4i + l / 16.  Keys at or past
-  // past + T read as zero (descriptor bound) and are masked.
-  const int64_t slab = ((int64_t)b * a.lkv + kvh) * a.S_max * 128;
-  const uint32_t valid_bytes = (uint32_t)(a.past + a.T) * 256u;
-  const i32x4 rk = buffer_rsrc(a.k_cache + slab, valid_bytes);
-  const i32x4 rv = buffer_rsrc(a.v_cache + slab, valid_bytes);
-  unsigned char* ring = smem + wave * kWaveRingB;
-  // a stage: K of tile kt and V of tile kt (PIPE: of tile kt - 1).  A tile
-  // outside the wave's range may be loaded and is never read; below key 0
-  // the offset wraps past the descriptor bound and reads zero.
-  auto dma_tile = [&](int kt, int st) {
-    const uint32_t base = lds_addr(ring + st * kStageB);
-    const int vt = PIPE ? kt - 1 : kt;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int key = 4 * i + (lane >> 4);
-      const uint32_t sw = (uint32_t)(((lane & 15) ^ kswz(key)) << 4);
-      dma16(rk, (uint32_t)(kt * kKeys + key) * 256u + sw, base + i * 1024);
-      dma16(rv, (uint32_t)(vt * kKeys + key) * 256u + sw, base + kTileB + i * 1024);
-    }
-  };
 
   f32x16 o[4];
 #pragma unroll
@@ -304,7 +312,7 @@ void attn_flash_kernel(AttnArgs a, int n_rb) {
     // tile w0 + i lives in stage i % NST; tiles up to i + NST - 1 are in
     // flight while tile i is computed.  The stage a load refills was read
     // by the previous tile: lgkmcnt(0) first.
-    for (int j = 0; j < NST - 1 && j < n; ++j) dma_tile(w0 + j, j);
+    for (int j = early ? 1 : 0; j < NST - 1 && j < n; ++j) dma_tile(w0 + j, j);
     for (int i = 0; i < n; ++i) {
       if (i + NST - 1 < n) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
