@@ -99,16 +99,22 @@ constexpr int gemm_waves_per_simd(int bm, int bn, int nw, int stages, int bk = 6
   return (nw / 4 < 1 ? 1 : nw / 4) * (163840 / (stages * (bm + bn) * bk * 2));
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M, int S, int BK = 64>
+// MF16: v_mfma_f32_16x16x32_bf16 on 16x16 output blocks instead of
+// v_mfma_f32_32x32x16_bf16 on 32x32 ones (the launch picks it for the
+// weight-streaming GEMMs of few rows, where it measured 2-7% faster; on the
+// 256-row prefill tiles its larger operand sets ran out of registers).
+template <int BM, int BN, int WGM, int WGN, int EPI, bool SPLIT, int GROUP_M, int S, int BK = 64, bool MF16 = false>
 __global__ __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd(BM, BN, WGM * WGN, S, BK),
                                    gemm_waves_per_simd(BM, BN, WGM * WGN, S, BK))))
 void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int BW = MF16 ? 16 : 32;         // output block edge of one MFMA
+  constexpr int NE = BW * BW / 64;           // accumulator values per lane and block
+  constexpr int TM = WM / BW, TN = WN / BW;
   constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
-  static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 block");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile in whole 32-row / 32-column units");
   static_assert(EPI != EPI_SILU_BF16 || (TN % 2 == 0), "silu pairs need an even number of n-blocks");
   // bf16 outputs accumulate C^T (B fragment as the first MFMA operand): a
   // lane then holds four consecutive output columns of one row, staged by
@@ -209,165 +215,302 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       if (k0 + lc * 8 >= kend) *reinterpret_cast<u32x4*>(st + row * BK + swz<BK>(row, lc) * 8) = u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // tile-local column of the j-th 32-wide n-block of this wave
+  // tile-local column of the j-th BW-wide n-block of this wave
   auto ncol = [&](int j) -> int {
     if (EPI == EPI_SILU_BF16)
-      return j < TN / 2 ? wn * (WN / 2) + j * 32 : BN / 2 + wn * (WN / 2) + (j - TN / 2) * 32;
-    return wn * WN + j * 32;
+      return j < TN / 2 ? wn * (WN / 2) + j * BW : BN / 2 + wn * (WN / 2) + (j - TN / 2) * BW;
+    return wn * WN + j * BW;
   };
 
-  f32x16 acc[TM][TN];
+  using AccT = std::conditional_t<MF16, f32x4, f32x16>;
+  AccT acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < NE; ++e) acc[i][j][e] = 0.f;
 
-  const int lr = lane & 31, lh = lane >> 5;
-  bf16x8 af[2][TM], bfr[2][TN];
-  // One K block is KS k-steps of 16.  Each k-step's MFMAs go out two at a
-  // time in a fenced, hand-ordered stream (sched_barrier keeps it): after
-  // each pair come the operand reads of the following k-step and, in the
-  // first k-step, slices of a later block's direct-to-LDS loads.  In the
-  // last k-step the wave waits for the next block (vmcnt, then a barrier)
-  // after half of its MFMAs, and reads the next block's first operands
-  // under the other half, so a block boundary leaves no gap in the matrix
-  // pipe.  Fragment set ks & 1 holds k-step ks (KS is even).
-  constexpr int KS = BK / 16;
-  static_assert(KS % 2 == 0, "fragment sets alternate per k-step");
-  constexpr int NF = TM + TN, NMF = TM * TN;
-  constexpr int NPAIR = (NMF + 1) / 2;
-  constexpr int RDP = (NF + NPAIR - 1) / NPAIR;   // operand reads after each MFMA pair
-  constexpr int H1 = NPAIR / 2;                    // pairs of the last k-step before the wait
-  constexpr int RDP2 = (NF + (NPAIR - H1) - 1) / (NPAIR - H1);
-  auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int fs, int x) {
-    // order A0, B0..B(TN-1), A1..A(TM-1): the next k-step's first MFMAs
-    // need A0 with every B
-    const int c = ks * 2 + lh;
-    if (x == 0 || x > TN) {
-      const int i = x == 0 ? 0 : x - TN;
-      const int row = wm * WM + i * 32 + lr;
-      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
-    } else {
-      const int row = ncol(x - 1) + lr;
-      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
-    }
-  };
-  auto mfma_pair = [&](int fs, int pr) {
-#pragma unroll
-    for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m) {
-      if constexpr (TR)
-        acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fs][m % TN], af[fs][m / TN],
-                                                                    acc[m / TN][m % TN], 0, 0, 0);
-      else
-        acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
-                                                                    acc[m / TN][m % TN], 0, 0, 0);
-    }
-  };
-  const bool tail = (kend - kbeg) % BK != 0;
-  auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
-  // A bare s_barrier, not __syncthreads(): the latter's workgroup release
-  // fence waits for every outstanding direct-to-LDS load (vmcnt(0)), which
-  // would collapse the ring to one block in flight.  Before it each wave
-  // has waited (vmcnt) for its own loads of the block about to be read and
-  // (lgkmcnt) for its reads of the block just finished; the barrier makes
-  // both true for all waves, so the block can be read and the stage it
-  // frees can be refilled.  The asm memory clobber keeps the compiler from
-  // moving LDS accesses across it.
-  auto settle = [&](int blk) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-    if (tail && blk == nk - 1) {
-      zero_tail(blk % S, kblk(blk));
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // the zero stores are done
+  // lane lr of a block edge; lh: the lane's group (k values 8 lh .. 8 lh + 7
+  // of an operand, rows 4 lh .. of an output block)
+  const int lr = lane & (BW - 1), lh = lane / BW;
+  if constexpr (MF16) {
+    // v_mfma_f32_16x16x32_bf16: lane l supplies row (or column) l & 15 of a
+    // 16-row operand block and its k values 8 (l >> 4) .. + 7 of the k-step's
+    // 32.  One K block is KS k-steps of 32.  A fragments come in two sets
+    // (set ks & 1 holds k-step ks; the next k-step's are read while this
+    // one's MFMAs run), B fragments in one: the MFMAs go out column by
+    // column (B fragment j with every A fragment), and each B fragment is
+    // refilled for the next k-step right after its last MFMA.  The stream is
+    // fenced (sched_barrier) per column; the first k-step also carries
+    // slices of a later block's direct-to-LDS loads.  In the last k-step the
+    // wave waits for the next block (vmcnt, then a barrier) after half of its
+    // columns, then reads the next block's A fragments and the B fragments
+    // already used, and the rest as their columns finish, so a block boundary
+    // leaves no gap in the matrix pipe.
+    bf16x8 fa[2][TM], fb[TN];
+    constexpr int KS = BK / 32;
+    static_assert(KS % 2 == 0, "A fragment sets alternate per k-step");
+    static_assert(TN >= TM, "the next k-step's A reads follow the first TM columns");
+    constexpr int JW = TN / 2;                 // columns of the last k-step before the wait
+    auto rdA = [&](const bf16* sA, int ks, int set, int i) {
+      const int row = wm * WM + i * 16 + lr, c = ks * 4 + lh;
+      fa[set][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
+    };
+    auto rdB = [&](const bf16* sB, int ks, int j) {
+      const int row = ncol(j) + lr, c = ks * 4 + lh;
+      fb[j] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
+    };
+    auto mfma_col = [&](int set, int j) {
+  #pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (TR)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[set][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[set][i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    const bool tail = (kend - kbeg) % BK != 0;
+    auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
+    // A bare s_barrier, not __syncthreads(): the latter's workgroup release
+    // fence waits for every outstanding direct-to-LDS load (vmcnt(0)), which
+    // would collapse the ring to one block in flight.  Before it each wave
+    // has waited (vmcnt) for its own loads of the block about to be read and
+    // (lhkmcnt) for its reads of the block just finished; the barrier makes
+    // both true for all waves, so the block can be read and the stage it
+    // frees can be refilled.  The asm memory clobber keeps the compiler from
+    // moving LDS accesses across it.
+    auto settle = [&](int blk) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lhkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
-    }
-  };
-  // One block from stage kt % S.  DMA: this block issues block kt + S - 1
-  // (steady state); NEXT: a block kt + 1 follows; SD: the steady-state
-  // wait (S - 2 blocks may stay in flight) rather than vmcnt(0).
-  auto block = [&](auto dma_tag, auto next_tag, int kt) {
-    constexpr bool DMA = decltype(dma_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;
-    const int cur = kt % S;
-    const bf16* sA = smem + cur * STAGE;
-    const bf16* sB = sA + BM * BK;
-    const int nxt = (kt + 1) % S;
-    const bf16* nA = smem + nxt * STAGE;
-    const bf16* nB = nA + BM * BK;
-    const int64_t dk0 = kblk(kt + S - 1);
-    const int dbuf = (kt + S - 1) % S;
-    __builtin_amdgcn_sched_barrier(0);
-    int v = 0;
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-#pragma unroll
-      for (int pr = 0; pr < NPAIR; ++pr) {
-        mfma_pair(ks & 1, pr);
-#pragma unroll
-        for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
-        if constexpr (DMA) {
-          if (ks == 0) {
-            while (v < NV && (pr + 1) * NV >= (v + 1) * NPAIR) dma_slice(v++, dk0, dbuf);
+      if (tail && blk == nk - 1) {
+        zero_tail(blk % S, kblk(blk));
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // the zero stores are done
+        asm volatile("s_barrier" ::: "memory");
+      }
+    };
+    // One block from stage kt % S.  DMA: this block issues block kt + S - 1
+    // (steady state); NEXT: a block kt + 1 follows.
+    auto block = [&](auto dma_tag, auto next_tag, int kt) {
+      constexpr bool DMA = decltype(dma_tag)::value;
+      constexpr bool NEXT = decltype(next_tag)::value;
+      const int cur = kt % S;
+      const bf16* sA = smem + cur * STAGE;
+      const bf16* sB = sA + BM * BK;
+      const int nxt = (kt + 1) % S;
+      const bf16* nA = smem + nxt * STAGE;
+      const bf16* nB = nA + BM * BK;
+      const int64_t dk0 = kblk(kt + S - 1);
+      const int dbuf = (kt + S - 1) % S;
+      __builtin_amdgcn_sched_barrier(0);
+      int v = 0;
+  #pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+  #pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          mfma_col(ks & 1, j);
+          rdB(sB, ks + 1, j);
+          if (j < TM) rdA(sA, ks + 1, (ks + 1) & 1, j);
+          if constexpr (DMA) {
+            if (ks == 0) {
+              while (v < NV && (j + 1) * NV >= (v + 1) * TN) dma_slice(v++, dk0, dbuf);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  #pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        mfma_col((KS - 1) & 1, j);
+        if constexpr (NEXT) {
+          if (j == JW - 1) {
+            if constexpr (DMA)
+              wait_vm<(S - 2) * NV>();
+            else
+              wait_vm0();
+            settle(kt + 1);
+            __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+            for (int i = 0; i < TM; ++i) rdA(nA, 0, 0, i);
+  #pragma unroll
+            for (int jj = 0; jj < JW; ++jj) rdB(nB, 0, jj);
+          } else if (j >= JW) {
+            rdB(nB, 0, j);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-#pragma unroll
-    for (int pr = 0; pr < H1; ++pr) {
-      mfma_pair(1, pr);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (NEXT) {
-      if constexpr (DMA)
+    };
+
+    // Pipeline: blocks 0 .. S-2 are issued up front; block kt issues block
+    // kt + S - 1 in its first k-step and waits for block kt + 1 in its last
+    // (vmcnt counts this wave's outstanding loads, which complete in issue
+    // order).
+    if (nk > 0) {
+      const int pro = nk < S - 1 ? nk : S - 1;
+      for (int blk = 0; blk < pro; ++blk)
+  #pragma unroll
+        for (int v = 0; v < NV; ++v) dma_slice(v, kblk(blk), blk);
+      if (pro - 1 == S - 2)
         wait_vm<(S - 2) * NV>();
       else
         wait_vm0();
-      settle(kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
+      settle(0);
+  #pragma unroll
+      for (int i = 0; i < TM; ++i) rdA(smem, 0, 0, i);
+  #pragma unroll
+      for (int j = 0; j < TN; ++j) rdB(smem + BM * BK, 0, j);
     }
-#pragma unroll
-    for (int pr = H1; pr < NPAIR; ++pr) {
-      mfma_pair(1, pr);
-      if constexpr (NEXT) {
-#pragma unroll
-        for (int x = (pr - H1) * RDP2; x < (pr - H1) * RDP2 + RDP2 && x < NF; ++x) read_frag(nA, nB, 0, 0, x);
+    int kt = 0;
+    for (; kt + S - 1 < nk; ++kt) block(std::true_type{}, std::true_type{}, kt);      // steady state
+    for (; kt + 1 < nk; ++kt) block(std::false_type{}, std::true_type{}, kt);         // drain
+    if (kt < nk) block(std::false_type{}, std::false_type{}, kt);                     // last block
+  } else {
+    bf16x8 af[2][TM], bfr[2][TN];
+    // One K block is KS k-steps of 16.  Each k-step's MFMAs go out two at a
+    // time in a fenced, hand-ordered stream (sched_barrier keeps it): after
+    // each pair come the operand reads of the following k-step and, in the
+    // first k-step, slices of a later block's direct-to-LDS loads.  In the
+    // last k-step the wave waits for the next block (vmcnt, then a barrier)
+    // after half of its MFMAs, and reads the next block's first operands
+    // under the other half, so a block boundary leaves no gap in the matrix
+    // pipe.  Fragment set ks & 1 holds k-step ks (KS is even).
+    constexpr int KS = BK / 16;
+    static_assert(KS % 2 == 0, "fragment sets alternate per k-step");
+    constexpr int NF = TM + TN, NMF = TM * TN;
+    constexpr int NPAIR = (NMF + 1) / 2;
+    constexpr int RDP = (NF + NPAIR - 1) / NPAIR;   // operand reads after each MFMA pair
+    constexpr int H1 = NPAIR / 2;                    // pairs of the last k-step before the wait
+    constexpr int RDP2 = (NF + (NPAIR - H1) - 1) / (NPAIR - H1);
+    auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int fs, int x) {
+      // order A0, B0..B(TN-1), A1..A(TM-1): the next k-step's first MFMAs
+      // need A0 with every B
+      const int c = ks * 2 + lh;
+      if (x == 0 || x > TN) {
+        const int i = x == 0 ? 0 : x - TN;
+        const int row = wm * WM + i * 32 + lr;
+        af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
+      } else {
+        const int row = ncol(x - 1) + lr;
+        bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
       }
+    };
+    auto mfma_pair = [&](int fs, int pr) {
+  #pragma unroll
+      for (int m = 2 * pr; m < 2 * pr + 2 && m < NMF; ++m) {
+        if constexpr (TR)
+          acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fs][m % TN], af[fs][m / TN],
+                                                                      acc[m / TN][m % TN], 0, 0, 0);
+        else
+          acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fs][m / TN], bfr[fs][m % TN],
+                                                                      acc[m / TN][m % TN], 0, 0, 0);
+      }
+    };
+    const bool tail = (kend - kbeg) % BK != 0;
+    auto kblk = [&](int blk) { return kbeg + (int64_t)blk * BK; };
+    // A bare s_barrier, not __syncthreads(): the latter's workgroup release
+    // fence waits for every outstanding direct-to-LDS load (vmcnt(0)), which
+    // would collapse the ring to one block in flight.  Before it each wave
+    // has waited (vmcnt) for its own loads of the block about to be read and
+    // (lgkmcnt) for its reads of the block just finished; the barrier makes
+    // both true for all waves, so the block can be read and the stage it
+    // frees can be refilled.  The asm memory clobber keeps the compiler from
+    // moving LDS accesses across it.
+    auto settle = [&](int blk) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      if (tail && blk == nk - 1) {
+        zero_tail(blk % S, kblk(blk));
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // the zero stores are done
+        asm volatile("s_barrier" ::: "memory");
+      }
+    };
+    // One block from stage kt % S.  DMA: this block issues block kt + S - 1
+    // (steady state); NEXT: a block kt + 1 follows; SD: the steady-state
+    // wait (S - 2 blocks may stay in flight) rather than vmcnt(0).
+    auto block = [&](auto dma_tag, auto next_tag, int kt) {
+      constexpr bool DMA = decltype(dma_tag)::value;
+      constexpr bool NEXT = decltype(next_tag)::value;
+      const int cur = kt % S;
+      const bf16* sA = smem + cur * STAGE;
+      const bf16* sB = sA + BM * BK;
+      const int nxt = (kt + 1) % S;
+      const bf16* nA = smem + nxt * STAGE;
+      const bf16* nB = nA + BM * BK;
+      const int64_t dk0 = kblk(kt + S - 1);
+      const int dbuf = (kt + S - 1) % S;
       __builtin_amdgcn_sched_barrier(0);
+      int v = 0;
+  #pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+  #pragma unroll
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          mfma_pair(ks & 1, pr);
+  #pragma unroll
+          for (int x = pr * RDP; x < pr * RDP + RDP && x < NF; ++x) read_frag(sA, sB, ks + 1, (ks + 1) & 1, x);
+          if constexpr (DMA) {
+            if (ks == 0) {
+              while (v < NV && (pr + 1) * NV >= (v + 1) * NPAIR) dma_slice(v++, dk0, dbuf);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  #pragma unroll
+      for (int pr = 0; pr < H1; ++pr) {
+        mfma_pair(1, pr);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (NEXT) {
+        if constexpr (DMA)
+          wait_vm<(S - 2) * NV>();
+        else
+          wait_vm0();
+        settle(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  #pragma unroll
+      for (int pr = H1; pr < NPAIR; ++pr) {
+        mfma_pair(1, pr);
+        if constexpr (NEXT) {
+  #pragma unroll
+          for (int x = (pr - H1) * RDP2; x < (pr - H1) * RDP2 + RDP2 && x < NF; ++x) read_frag(nA, nB, 0, 0, x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Pipeline: blocks 0 .. S-2 are issued up front; block kt issues block
+    // kt + S - 1 in its first k-step and waits for block kt + 1 in its last
+    // (vmcnt counts this wave's outstanding loads, which complete in issue
+    // order).
+    if (nk > 0) {
+      const int pro = nk < S - 1 ? nk : S - 1;
+      for (int blk = 0; blk < pro; ++blk)
+  #pragma unroll
+        for (int v = 0; v < NV; ++v) dma_slice(v, kblk(blk), blk);
+      if (pro - 1 == S - 2)
+        wait_vm<(S - 2) * NV>();
+      else
+        wait_vm0();
+      settle(0);
+  #pragma unroll
+      for (int x = 0; x < NF; ++x) read_frag(smem, smem + BM * BK, 0, 0, x);
     }
-  };
-
-  // Pipeline: blocks 0 .. S-2 are issued up front; block kt issues block
-  // kt + S - 1 in its first k-step and waits for block kt + 1 in its last
-  // (vmcnt counts this wave's outstanding loads, which complete in issue
-  // order).
-  if (nk > 0) {
-    const int pro = nk < S - 1 ? nk : S - 1;
-    for (int blk = 0; blk < pro; ++blk)
-#pragma unroll
-      for (int v = 0; v < NV; ++v) dma_slice(v, kblk(blk), blk);
-    if (pro - 1 == S - 2)
-      wait_vm<(S - 2) * NV>();
-    else
-      wait_vm0();
-    settle(0);
-#pragma unroll
-    for (int x = 0; x < NF; ++x) read_frag(smem, smem + BM * BK, 0, 0, x);
+    int kt = 0;
+    for (; kt + S - 1 < nk; ++kt) block(std::true_type{}, std::true_type{}, kt);      // steady state
+    for (; kt + 1 < nk; ++kt) block(std::false_type{}, std::true_type{}, kt);         // drain
+    if (kt < nk) block(std::false_type{}, std::false_type{}, kt);                     // last block
   }
-  int kt = 0;
-  for (; kt + S - 1 < nk; ++kt) block(std::true_type{}, std::true_type{}, kt);      // steady state
-  for (; kt + 1 < nk; ++kt) block(std::false_type{}, std::true_type{}, kt);         // drain
-  if (kt < nk) block(std::false_type{}, std::false_type{}, kt);                     // last block
 
-  // ---- epilogue.  MFMA layout: lane holds column (lane & 31) and rows
-  // 8*(e/4) + 4*(lane/32) + e%4 of each 32x32 block (transposed for TR).
+  // ---- epilogue.  MFMA layout: lane holds column lr = lane % BW and rows
+  // 8*(e/4) + 4*lh + e%4 of each BW x BW block, lh = lane / BW (for BW = 16
+  // that is rows 4*lh + e, e < 4; transposed for TR).
   if constexpr (EPI == EPI_ARGMAX) {
     // Greedy-decode candidates: per tile row, the largest bf16-rounded
     // value over the tile's columns and the first column holding it (ties
-    // to the smaller column, as argmax takes the first maximum); the 32
-    // lanes of a half-wave hold 32 columns of a row, then the WGN waves of
+    // to the smaller column, as argmax takes the first maximum); the BW
+    // lanes of a lane group hold BW columns of a row, then the WGN waves of
     // the tile combine through LDS.
     static_assert(!SPLIT, "argmax candidates come from whole K");
     __syncthreads();   // the ring is no longer read
@@ -377,7 +520,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < NE; ++e) {
         float bv = -INFINITY;
         int bi = -1;
 #pragma unroll
@@ -389,9 +532,12 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
             bi = (int)(p.col0 + col);
           }
         }
-        cand_best32(bv, bi);
+        if constexpr (MF16)
+          cand_best16(bv, bi);
+        else
+          cand_best32(bv, bi);
         if (lr == 0) {
-          const int r = wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+          const int r = wm * WM + i * BW + 8 * (e >> 2) + 4 * lh + (e & 3);
           cv[wn * BM + r] = bv;
           ci[wn * BM + r] = bi;
         }
@@ -414,10 +560,11 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   if constexpr (EPI == EPI_QKV) {
     static_assert(qkv_tile_ok(BM, BN, S, BK), "QKV tile must cover whole heads and fit the ring");
     // one head (128 columns) at a time: stage its fp32 columns [BM][128] in
-    // LDS (16-byte chunk c of row r at c ^ ((r >> 2) & 1): the two
-    // half-waves write rows 4 apart), then finish it 16 lanes per row
+    // LDS (column c of row r at c ^ BW * ((r / 4) % (64 / BW)): the 64 / BW
+    // lane groups of a block write rows 4 apart, and land on different
+    // banks), then finish it 16 lanes per row
     float* st = reinterpret_cast<float*>(smem);
-    auto st_off = [&](int r, int c) -> int { return r * 128 + ((((c >> 2) ^ (r >> 2)) & 1) | ((c >> 2) & ~1)) * 4 + (c & 3); };
+    auto st_off = [&](int r, int c) -> int { return r * 128 + (c ^ (BW * ((r >> 2) & (64 / BW - 1)))); };
     const int j16 = tid & 15;
     const RopeCoef rc = rope_coef(p.qkv.theta, j16);
     constexpr int HPT = BN / 128;                      // heads per tile
@@ -432,8 +579,8 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            st[st_off(wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3), c0 - hh * 128 + lr)] = acc[i][j][e];
+          for (int e = 0; e < NE; ++e)
+            st[st_off(wm * WM + i * BW + 8 * (e >> 2) + 4 * lh + (e & 3), c0 - hh * 128 + lr)] = acc[i][j][e];
       }
       __syncthreads();
       const int h = tn * HPT + hh;
@@ -458,8 +605,8 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t gm = m0 + wm * WM + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        for (int e = 0; e < NE; ++e) {
+          const int64_t gm = m0 + wm * WM + i * BW + 8 * (e >> 2) + 4 * lh + (e & 3);
           if (full || (gm < M && gn < p.N)) C[gm * p.ldc + gn] = acc[i][j][e];
         }
     }
@@ -489,13 +636,13 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   // accesses run in order, so it needs no wait.
 #pragma unroll
   for (int ps = 0; ps < WM / PR; ++ps) {
-  // (C^T layout: row i * 32 + lr, columns j * 32 + 8 * g4 + 4 * lh .. + 3)
+  // (C^T layout: row i * BW + lr, columns j * BW + 8 * g4 + 4 * lh .. + 3)
 #pragma unroll
   for (int j = 0; j < (EPI == EPI_SILU_BF16 ? TN / 2 : TN); ++j)
 #pragma unroll
-    for (int i = ps * (PR / 32); i < (ps + 1) * (PR / 32); ++i)
+    for (int i = ps * (PR / BW); i < (ps + 1) * (PR / BW); ++i)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
+      for (int g4 = 0; g4 < NE / 4; ++g4) {
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -507,7 +654,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
             v[q] = acc[i][j][e];
           }
         }
-        *reinterpret_cast<u32x2*>(so + so_idx(i * 32 - ps * PR + lr, j * 32 + 8 * g4 + 4 * lh)) =
+        *reinterpret_cast<u32x2*>(so + so_idx(i * BW - ps * PR + lr, j * BW + 8 * g4 + 4 * lh)) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
@@ -1079,7 +1226,7 @@ void mark_gemm(hipStream_t s, const char* kern, int bm, int bn, int stages, int 
 
 // finish = false: a split plan stops after the partials (the consumer sums
 // them itself)
-template <int BM, int BN, int WGM, int WGN, int S>
+template <int BM, int BN, int WGM, int WGN, int S, bool MF16 = false>
 hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s,
                        bool finish = true) {
   constexpr int NT = WGM * WGN * 64;
@@ -1089,7 +1236,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     q.C = scratch;
     q.ldc = p.N;
     dim3 grid(pl.tiles_m * pl.tiles_n, pl.splits);
-    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
+    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, true, GM, S, 64, MF16><<<grid, NT, 0, s>>>(q, pl.tiles_m, pl.tiles_n, pl.kps);
     mark_gemm(s, "gemm_splitk", BM, BN, S, epi, p);
     if (!finish) return hipGetLastError();
     const int64_t cols = epi == EPI_SILU_BF16 ? p.li : p.N;
@@ -1111,14 +1258,14 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   dim3 grid(pl.tiles_m * pl.tiles_n);
   if constexpr ((BN / WGN / 32) % 2 == 0) {
     if (epi == EPI_SILU_BF16) {
-      gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
       mark_gemm(s, "gemm_tile", BM, BN, S, EPI_SILU_BF16, p);
       return hipGetLastError();
     }
   }
   if constexpr (qkv_tile_ok(BM, BN, S)) {
     if (epi == EPI_QKV) {
-      gemm_kernel<BM, BN, WGM, WGN, EPI_QKV, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      gemm_kernel<BM, BN, WGM, WGN, EPI_QKV, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
       mark_gemm(s, "gemm_tile", BM, BN, S, EPI_QKV, p);
       return hipGetLastError();
     }
@@ -1127,16 +1274,16 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
     if constexpr (!plain_out_only(BN)) {
-      gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+      gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
       mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX, p);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
   }
   if (epi == EPI_BF16)
-    gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+    gemm_kernel<BM, BN, WGM, WGN, EPI_BF16, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   else
-    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, false, GM, S><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
+    gemm_kernel<BM, BN, WGM, WGN, EPI_F32, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
   mark_gemm(s, "gemm_tile", BM, BN, S, epi, p);
   return hipGetLastError();
 }
@@ -1285,18 +1432,27 @@ int64_t gemm_argmax_tiles_n(int64_t M, int64_t N, int64_t K) {
 
 namespace {
 
+// Problems of at most this many rows (decode batches: the weight stream)
+// run the small tiles in the 16x16x32 form.
+constexpr int64_t kMf16Rows = 256;
+template <int BM, int BN, int WGM, int WGN, int S>
+hipError_t launch_rows(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s, bool finish) {
+  if (p.M <= kMf16Rows) return launch_tile<BM, BN, WGM, WGN, S, true>(p, epi, pl, scratch, s, finish);
+  return launch_tile<BM, BN, WGM, WGN, S, false>(p, epi, pl, scratch, s, finish);
+}
+
 hipError_t launch_plan(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s,
                        bool finish = true) {
   switch (pl.v) {
     case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, epi, pl, scratch, s, finish);
     case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, epi, pl, scratch, s, finish);
-    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, epi, pl, scratch, s, finish);
-    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, epi, pl, scratch, s, finish);
-    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, epi, pl, scratch, s, finish);
-    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, epi, pl, scratch, s, finish);
-    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, epi, pl, scratch, s, finish);
+    case V128x128_4: return launch_rows<128, 128, 4, 2, 4>(p, epi, pl, scratch, s, finish);
+    case V128x128_2: return launch_rows<128, 128, 4, 2, 2>(p, epi, pl, scratch, s, finish);
+    case V128x64_3: return launch_rows<128, 64, 4, 1, 3>(p, epi, pl, scratch, s, finish);
+    case V128x64_6: return launch_rows<128, 64, 4, 1, 6>(p, epi, pl, scratch, s, finish);
+    case V64x128_3: return launch_rows<64, 128, 2, 2, 3>(p, epi, pl, scratch, s, finish);
     case V256x320: return launch_tile<256, 320, 4, 2, 2>(p, epi, pl, scratch, s, finish);
-    default: return launch_tile<64, 64, 2, 2, 8>(p, epi, pl, scratch, s, finish);
+    default: return launch_rows<64, 64, 2, 2, 8>(p, epi, pl, scratch, s, finish);
   }
 }
 
@@ -1338,13 +1494,13 @@ hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, b
   switch (pl.v) {
     case V256x256: return launch_tile<256, 256, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, !split);
     case V256x128: return launch_tile<256, 128, 4, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
-    case V128x128_4: return launch_tile<128, 128, 4, 2, 4>(p, EPI_QKV, pl, scratch, s, !split);
-    case V128x128_2: return launch_tile<128, 128, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, !split);
-    case V128x64_3: return launch_tile<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, !split);
-    case V128x64_6: return launch_tile<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, !split);
-    case V64x128_3: return launch_tile<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x128_4: return launch_rows<128, 128, 4, 2, 4>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x128_2: return launch_rows<128, 128, 4, 2, 2>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x64_3: return launch_rows<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, !split);
+    case V128x64_6: return launch_rows<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, !split);
+    case V64x128_3: return launch_rows<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
     case V256x320: return hipErrorInvalidValue;   // never planned for QKV
-    default: return launch_tile<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, !split);
+    default: return launch_rows<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, !split);
   }
 }
 
