@@ -185,6 +185,19 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
   const int trg = lane >> 4, tri = lane & 15;
   const int tr_key = 4 * (trg >> 1) + (tri >> 2);          // + kb*32 + sub*16 + rd*8
   const int tr_d = (trg & 1) * 16 + 4 * (tri & 3);         // + db*32
+  // The key swizzle depends only on a key's low four bits, so the read
+  // offsets of keys 16 apart differ by a constant: the per-lane offsets are
+  // computed once (V^T: keys tr_key and tr_key + 8 of each 32-wide d block;
+  // K: row lr of each 16-wide k-step) and the tile loop adds immediates.
+  uint32_t vbo[4][2], kbo[8];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = db * 32 + tr_d;
+    vbo[db][0] = toff(tr_key, d >> 3) + ((d >> 2) & 1) * 8;
+    vbo[db][1] = toff(tr_key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kbo[ks] = toff(lr, ks * 2 + lh);
   auto compute = [&](int kt, auto st) {
     const unsigned char* K = stage(st);
     const unsigned char* V = K + kTile;
@@ -199,7 +212,7 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + toff(kb * 32 + lr, ks * 2 + lh));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + kbo[ks] + kb * 8192);
 #pragma unroll
         for (int hw = 0; hw < HW; ++hw)
           s[hw][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[hw][ks], s[hw][kb], 0, 0, 0);
@@ -259,10 +272,8 @@ void attn_prefill_kernel(AttnArgs a, PrefillPlan p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-          const int key = kb * 32 + sub * 16 + tr_key;
-          const int d = db * 32 + tr_d;
-          const uint32_t a0 = toff(key, d >> 3) + ((d >> 2) & 1) * 8;
-          const uint32_t a1 = toff(key + 8, d >> 3) + ((d >> 2) & 1) * 8;
+          const uint32_t a0 = vbo[db][0] + (uint32_t)((kb * 32 + sub * 16) * 256);
+          const uint32_t a1 = vbo[db][1] + (uint32_t)((kb * 32 + sub * 16) * 256);
           const lds_bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a0));
           const lds_bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) lds_bf16x4*)(V + a1));
           vf[db][kb][sub] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
