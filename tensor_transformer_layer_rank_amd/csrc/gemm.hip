@@ -115,7 +115,15 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   constexpr int TM = WM / BW, TN = WN / BW;
   constexpr int KC = BK / 8;                 // 16-byte chunks per tile row
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile in whole 32-row / 32-column units");
-  static_assert(EPI != EPI_SILU_BF16 || (TN % 2 == 0), "silu pairs need an even number of n-blocks");
+  // SiLU tiles hold gate and up rows in one of two layouts: with an even
+  // number of 32-column blocks per wave, gate rows in the tile's first half
+  // and up rows in its second (block j pairs with block j + TN / 2); with an
+  // odd number (256 x 320 tiles: 5 per wave), each 32-row block holds 16
+  // gate rows and the 16 matching up rows (SI), so that in the C^T
+  // accumulator layout a lane's values e < 8 are gate sums and e + 8 the
+  // up sums of the same output
+  constexpr bool SI = EPI == EPI_SILU_BF16 && TN % 2 == 1;
+  static_assert(!SI || !MF16, "the interleaved silu layout needs 32x32 blocks");
   // bf16 outputs accumulate C^T (B fragment as the first MFMA operand): a
   // lane then holds four consecutive output columns of one row, staged by
   // one 8-byte LDS write
@@ -185,8 +193,12 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   for (int v = 0; v < NV; ++v) {
     const bool isA = v < A_G;
     const int g = wave + (isA ? v : v - A_G) * NW;
-    const bool up = !isA && EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
-    const int row = g * RPI + grow - (up ? BN / 2 : 0);
+    // SI: LDS row 32 b + r (r < 16) holds gate row 16 b + r, 32 b + 16 + r
+    // the up row 16 b + r; the chunk swizzle has a period of 16 rows, so it
+    // is the same for the source row and the LDS row
+    const bool up = !isA && EPI == EPI_SILU_BF16 && (SI ? ((g * RPI) & 16) != 0 : g * RPI >= BN / 2);
+    const int row = SI && !isA ? (g * RPI + grow) / 32 * 16 + (g * RPI + grow) % 16
+                               : g * RPI + grow - (up ? BN / 2 : 0);
     uint32_t base = (uint32_t)(row * (isA ? lda_b : ldb_b));
     if (isA && gather) {
       const int64_t src = m0 + row < M ? (int64_t)p.a_rows[m0 + row] : -1;
@@ -201,7 +213,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
     } else {
       const int g = wave_u + (v - A_G) * NW;
-      const bool up = EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
+      const bool up = EPI == EPI_SILU_BF16 && (SI ? ((g * RPI) & 16) != 0 : g * RPI >= BN / 2);
       dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
     }
   };
@@ -217,7 +229,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   };
   // tile-local column of the j-th BW-wide n-block of this wave
   auto ncol = [&](int j) -> int {
-    if (EPI == EPI_SILU_BF16)
+    if (EPI == EPI_SILU_BF16 && !SI)
       return j < TN / 2 ? wn * (WN / 2) + j * BW : BN / 2 + wn * (WN / 2) + (j - TN / 2) * BW;
     return wn * WN + j * BW;
   };
@@ -637,24 +649,27 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
 #pragma unroll
   for (int ps = 0; ps < WM / PR; ++ps) {
   // (C^T layout: row i * BW + lr, columns j * BW + 8 * g4 + 4 * lh .. + 3)
+  // (SI: block j gives output columns j * 16 + 8 * g4 + 4 * lh .. + 3 from
+  // its values e = 4 * g4 + q, e < 8, and e + 8)
 #pragma unroll
-  for (int j = 0; j < (EPI == EPI_SILU_BF16 ? TN / 2 : TN); ++j)
+  for (int j = 0; j < (EPI == EPI_SILU_BF16 && !SI ? TN / 2 : TN); ++j)
 #pragma unroll
     for (int i = ps * (PR / BW); i < (ps + 1) * (PR / BW); ++i)
 #pragma unroll
-      for (int g4 = 0; g4 < NE / 4; ++g4) {
+      for (int g4 = 0; g4 < (SI ? NE / 8 : NE / 4); ++g4) {
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int e = 4 * g4 + q;
           if (EPI == EPI_SILU_BF16) {
-            const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
+            const float g = acc[i][j][e], u = SI ? acc[i][j][e + 8] : acc[i][j + TN / 2][e];
             v[q] = g / (1.f + __expf(-g)) * u;
           } else {
             v[q] = acc[i][j][e];
           }
         }
-        *reinterpret_cast<u32x2*>(so + so_idx(i * BW - ps * PR + lr, j * BW + 8 * g4 + 4 * lh)) =
+        const int c = SI ? j * 16 + 8 * g4 + 4 * lh : j * BW + 8 * g4 + 4 * lh;
+        *reinterpret_cast<u32x2*>(so + so_idx(i * BW - ps * PR + lr, c)) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
@@ -1113,24 +1128,26 @@ struct Variant {
   int bm, bn, stages;
   int resident;        // workgroups one CU holds (LDS-limited)
   float t_kb_us;       // time per 64-wide K block per resident round at full load
-  bool silu;           // wave tile has an even number of 32-column blocks
+  bool silu;           // the tile can hold gate/up pairs
 };
 // V256x320: 256 x 320 tiles (waves of 64 x 160) for the row-parallel
 // projections, whose N = 5120 is 16 such tiles: at 4096 rows that is one
 // round of 256 tiles, where 256-wide tiles need 1.25 rounds (or a second
-// launch for the last 1024 columns).  Bf16 and fp32 outputs only (a
-// 320-wide tile holds neither whole 128-column heads nor gate/up pairs),
-// and only for single-round grids: longer grids keep the persistent kernel.
+// launch for the last 1024 columns); likewise the 32B gate_up (12800 SiLU
+// outputs, 160 per tile) is five whole rounds at 4096 rows, where 256-wide
+// tiles need 6.25.  Bf16, fp32 and SiLU outputs (a 320-wide tile does not
+// hold whole 128-column heads), and only grids of whole rounds: other long
+// grids keep the 256-wide tiles and the persistent kernel.
 enum VariantId {
   V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V256x320, V_COUNT
 };
 constexpr Variant kVariants[V_COUNT] = {
     {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.59f, true},
     {128, 128, 2, 2, 1.08f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
-    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.45f, false},
+    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.45f, true},
 };
-// the planner offers the 320-wide tile to plain outputs on one round only
-constexpr bool plain_out_only(int bn) { return bn == 320; }
+// the 320-wide tile: no QKV or argmax epilogue, whole rounds only
+constexpr bool wide_tile(int bn) { return bn == 320; }
 // Constants fitted to a sweep of every (variant, split) plan over the
 // decode, prefill, lm_head and decode-argmax shapes of the Qwen3-0.6B / 32B
 // shards on MI355X (27 shapes; the chosen plans are within 1% of the
@@ -1196,12 +1213,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
     for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
       if (sp > 1 && (!allow_split || !quad_cols || kblocks < 4 * sp)) break;
       if (epi == EPI_SILU_BF16 && !v.silu) continue;
-      if (plain_out_only(v.bn) && (epi == EPI_QKV || epi == EPI_ARGMAX)) continue;
+      if (wide_tile(v.bn) && (epi == EPI_QKV || epi == EPI_ARGMAX)) continue;
       if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
       const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn, consumer_sums) * (sp > 1 ? 1.05 : 1.0);
-      if (plain_out_only(v.bn) && tm * tn * sp > kCUs) continue;
+      if (wide_tile(v.bn) && tm * tn * sp > kCUs && (sp > 1 || (tm * tn) % kCUs != 0)) continue;
       if (c < best_cost * 0.999) {
         best_cost = c;
         const int64_t kps = sp == 1 ? K : ((kblocks + sp - 1) / sp) * 64;
@@ -1256,7 +1273,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
     return hipGetLastError();
   }
   dim3 grid(pl.tiles_m * pl.tiles_n);
-  if constexpr ((BN / WGN / 32) % 2 == 0) {
+  if constexpr ((BN / WGN / 32) % 2 == 0 || !MF16) {
     if (epi == EPI_SILU_BF16) {
       gemm_kernel<BM, BN, WGM, WGN, EPI_SILU_BF16, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
       mark_gemm(s, "gemm_tile", BM, BN, S, EPI_SILU_BF16, p);
@@ -1273,7 +1290,7 @@ hipError_t launch_tile(const GemmProblem& p, int epi, const Plan& pl, void* scra
   // the planner never picks a variant that cannot run the epilogue
   if (epi == EPI_SILU_BF16 || epi == EPI_QKV) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX) {
-    if constexpr (!plain_out_only(BN)) {
+    if constexpr (!wide_tile(BN)) {
       gemm_kernel<BM, BN, WGM, WGN, EPI_ARGMAX, false, GM, S, 64, MF16><<<grid, NT, 0, s>>>(p, pl.tiles_m, pl.tiles_n, p.K);
       mark_gemm(s, "gemm_tile", BM, BN, S, EPI_ARGMAX, p);
       return hipGetLastError();
@@ -1355,7 +1372,7 @@ Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_spli
   for (int vi = 0; vi < V_COUNT; ++vi) {
     const Variant& v = kVariants[vi];
     if (epi == EPI_SILU_BF16 && !v.silu) continue;
-    if (plain_out_only(v.bn)) continue;   // a single-round tile: no whole rounds to split off
+    if (wide_tile(v.bn)) continue;   // whole rounds only: nothing to split off
     if (epi == EPI_QKV && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
     int64_t tm, tn;
     plan_cost(v, M, N, K, epi, 1, &tm, &tn);

@@ -385,6 +385,34 @@ def test_mlp_wide_tile_ragged():
     assert relerr(f64(part), p_ref) <= TOL_BF16
 
 
+def test_mlp_wide_tile_silu_ragged():
+    """The gate_up + SiLU GEMM on 320-row weight tiles (160 outputs each, 16
+    gate rows beside their 16 up rows in every 32-row block), element by
+    element: 2504 local intermediate columns are 15 tiles and a 104-column
+    tail, 3900 rows 15 tiles and a 60-row tail, and hidden 1000 ends inside a
+    64-wide K block.  The kernel marks confirm the tile shape ran."""
+    w = dict(hidden=1000, intermediate=5008, n_q_heads=2, n_kv_heads=2, head_dim=128, vocab=0, tp=2)
+    wid, M = 121, 3900
+    W = synth.full_weights(wid, w)
+    rk = Rank(w, 1, {k: v.to(DEV) for k, v in W.items()})
+    oc = ocfg(w, 1)
+    gu = O.merge_gate_up(shard64(oc, O.W_GATE, W["gate"]), shard64(oc, O.W_UP, W["up"]))
+    down = shard64(oc, O.W_DOWN, W["down"])
+    x = synth.activations(wid, M, w["hidden"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    tp.tp_kernel_marks(ev)
+    try:
+        h, part = run_mlp(rk, x.to(DEV), M)
+        torch.cuda.synchronize()
+        names = tp.tp_kernel_mark_names()
+    finally:
+        tp.tp_kernel_marks([])
+    assert any(n.startswith("gemm_tile<256,320,2>/silu[3900x5008x1000]") for n in names), names
+    h_ref, p_ref = O.mlp(oc, synth.to_f64(x), gu, down)
+    assert relerr(f64(h), h_ref) <= TOL_BF16
+    assert relerr(f64(part), p_ref) <= TOL_BF16
+
+
 # ------------------------------------------------------------------ attention
 
 def make_cache(w, wid, rk, B, S_max, past, n_global_kv):
