@@ -402,7 +402,7 @@ def run_bench(args):
     dec_gbps = dec_bytes / ph["decode"] / 1e9
 
     # dominant kernel: the prefill gate_up GEMM with its SiLU epilogue
-    # (the first SiLU launch: with a tail schedule it covers the leading
+    # (the first SiLU launch: under a tail schedule it covers the leading
     # columns only, so its work is read from the launched M x N x K)
     gu_name, gu_t = find_kernel(kernels, "prefill", lambda s: "/silu[" in s and s.startswith("gemm_tile"))
     gm, gn, gk = gemm_dims(gu_name) if gu_name else (T, 2 * L.li, H)
@@ -410,8 +410,9 @@ def run_bench(args):
     gu_bytes = 2 * (gm * gk + gn * gk + gm * gn // 2)
     gu_traffic = traffic_from_profile(f"gate_up_gemm_{args.workload}_hbm_traffic.txt", "gemm.hip")
     gu_tflops = gu_flops / gu_t / 1e12 if gu_t else None
-    roofline = {"kernel": f"{gu_name} (tp_mlp gate_up + SiLU*up of prefill {T} x {2 * L.li} x {H}: "
-                          f"the launch over output columns [0, {gn // 2}) of {L.li})",
+    cover = (f"one launch over all {L.li} output columns" if gn // 2 >= L.li
+             else f"the launch over output columns [0, {gn // 2}) of {L.li}")
+    roofline = {"kernel": f"{gu_name} (tp_mlp gate_up + SiLU*up of prefill {T} x {2 * L.li} x {H}: {cover})",
                 "bound": "mfma", "achieved": round(gu_tflops, 1) if gu_tflops else None,
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tflops / MFMA_BF16_PEAK_TFLOPS, 4) if gu_tflops else None,

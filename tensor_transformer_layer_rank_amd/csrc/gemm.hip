@@ -82,6 +82,9 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
     dst = a.v_cache + (((int64_t)b * a.lkv + (h - a.lq - a.lkv)) * a.S_max + pos) * 128;
   store_head_lanes(dst, x, j);
 }
+// the 320-wide tile: no QKV or argmax epilogue, no row gather, whole rounds
+// of tiles only
+constexpr bool wide_tile(int bn) { return bn == 320; }
 // the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
 // (the epilogue stages the tile 128 columns -- one head -- at a time)
 constexpr bool qkv_tile_ok(int bm, int bn, int stages, int bk = 64) {
@@ -134,7 +137,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   __shared__ __attribute__((aligned(16))) bf16 smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = __builtin_amdgcn_readfirstlane(wave) / WGN, wn = __builtin_amdgcn_readfirstlane(wave) % WGN;
 
   // tile coordinates: XCD-contiguous, then GROUP_M m-tiles per n-column sweep
   int tm, tn;
@@ -179,42 +182,54 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   // B rows of this tile: [b_row0, +BN) or, for silu, [gate0, +BN/2) and [up0, +BN/2)
   const int64_t nrow0 = EPI == EPI_SILU_BF16 ? (int64_t)tn * (BN / 2) : (int64_t)tn * BN;
   const int64_t nrows = EPI == EPI_SILU_BF16 ? p.li - nrow0 : p.N - nrow0;
-  // A rows: the tile's own rows from m0, or (row gather) rows a_rows[m0 + r]
-  // of the whole A, a row past M or an index outside A at an offset past
-  // the descriptor's range (2^31 + a K offset below 2^23: zeros)
-  const bool gather = !SPLIT && EPI != EPI_QKV && p.a_rows != nullptr;
+  // A rows: the tile's own rows from m0, or (row gather, bf16 and argmax
+  // outputs on tiles up to 256 wide) rows a_rows[m0 + r] of the whole A, a
+  // row past M or an index outside A at an offset past the descriptor's
+  // range (2^31 + a K offset below 2^23: zeros)
+  constexpr bool GATHER_OK = !SPLIT && (EPI == EPI_BF16 || EPI == EPI_ARGMAX) && !wide_tile(BN);
+  const bool gather = GATHER_OK && p.a_rows != nullptr;
   const __amdgpu_buffer_rsrc_t ra =
       gather ? make_rsrc(p.A, p.a_total * lda_b) : make_rsrc(p.A + m0 * p.lda, (M - m0) * lda_b);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.B + ((p.up_off ? p.up_off : p.li) + nrow0) * p.ldb, nrows * ldb_b);
-  // per-slice lane offsets (bytes, column 0) and LDS destinations within a stage
-  uint32_t voff[NV];
+  // Slice offsets.  A slice's rows are its first source row R (wave-uniform)
+  // plus the lane's row grow; R % 16 is the same for every slice of a wave
+  // (slices lie NW * RPI rows apart, gate/up halves and blocks are whole
+  // multiples of 16 rows) and the chunk swizzle has a period of 16 rows, so
+  // a lane's offset is a per-lane part per operand plus R times the row
+  // pitch, which the scalar unit computes.
+  // SI: LDS row 32 b + r (r < 16) holds gate row 16 b + r, 32 b + 16 + r the
+  // up row 16 b + r.
+  auto b_up = [&](int g) { return EPI == EPI_SILU_BF16 && (SI ? ((g * RPI) & 16) != 0 : g * RPI >= BN / 2); };
+  auto src_row0 = [&](bool isA, int g) -> int {
+    if (isA) return g * RPI;
+    if (SI) return (g * RPI) / 32 * 16 + (g * RPI) % 16;
+    return g * RPI - (b_up(g) ? BN / 2 : 0);
+  };
+  static_assert(EPI != EPI_SILU_BF16 || (BN / 2) % 16 == 0, "gate/up halves in whole 16-row units");
+  const uint32_t lsw = (uint32_t)(swz<BK>(((wave_u * RPI) & 15) + grow, gpc) << 4);
+  const uint32_t lane_a = (uint32_t)(grow * lda_b) + lsw, lane_b = (uint32_t)(grow * ldb_b) + lsw;
+  // gathered A rows: one offset per slice and lane
+  uint32_t ga[GATHER_OK ? A_G : 1];
+  if constexpr (GATHER_OK) {
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const bool isA = v < A_G;
-    const int g = wave + (isA ? v : v - A_G) * NW;
-    // SI: LDS row 32 b + r (r < 16) holds gate row 16 b + r, 32 b + 16 + r
-    // the up row 16 b + r; the chunk swizzle has a period of 16 rows, so it
-    // is the same for the source row and the LDS row
-    const bool up = !isA && EPI == EPI_SILU_BF16 && (SI ? ((g * RPI) & 16) != 0 : g * RPI >= BN / 2);
-    const int row = SI && !isA ? (g * RPI + grow) / 32 * 16 + (g * RPI + grow) % 16
-                               : g * RPI + grow - (up ? BN / 2 : 0);
-    uint32_t base = (uint32_t)(row * (isA ? lda_b : ldb_b));
-    if (isA && gather) {
-      const int64_t src = m0 + row < M ? (int64_t)p.a_rows[m0 + row] : -1;
-      base = src >= 0 && src < p.a_total ? (uint32_t)(src * lda_b) : 0x80000000u;
+    for (int v = 0; v < A_G; ++v) {
+      const int row = (wave_u + v * NW) * RPI + grow;
+      const int64_t src = gather && m0 + row < M ? (int64_t)p.a_rows[m0 + row] : -1;
+      ga[v] = (src >= 0 && src < p.a_total ? (uint32_t)(src * lda_b) : 0x80000000u) + lsw;
     }
-    voff[v] = base + (uint32_t)(swz<BK>(row, gpc) << 4);
   }
   auto dma_slice = [&](int v, int64_t k0, int buf) {
     bf16* st = smem + buf * STAGE;
     const uint32_t ko = (uint32_t)(k0 * 2);
     if (v < A_G) {
-      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
+      const int g = wave_u + v * NW;
+      uint32_t off = lane_a + (uint32_t)(src_row0(true, g) * lda_b);
+      if constexpr (GATHER_OK) off = gather ? ga[v] : off;
+      dma16(ra, off + ko, st + g * RPI * BK);
     } else {
       const int g = wave_u + (v - A_G) * NW;
-      const bool up = EPI == EPI_SILU_BF16 && (SI ? ((g * RPI) & 16) != 0 : g * RPI >= BN / 2);
-      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
+      dma16(b_up(g) ? ru : rg, lane_b + (uint32_t)(src_row0(false, g) * ldb_b) + ko, st + BM * BK + g * RPI * BK);
     }
   };
   // The last block may end inside the 64-wide K window: its columns at or
@@ -246,6 +261,11 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   // lane lr of a block edge; lh: the lane's group (k values 8 lh .. 8 lh + 7
   // of an operand, rows 4 lh .. of an output block)
   const int lr = lane & (BW - 1), lh = lane / BW;
+  // An operand row a lane reads is lr plus a multiple of 16 (wave tiles,
+  // blocks and gate/up halves start on such rows), and the chunk swizzle has
+  // a period of 16 rows: a fragment's LDS offset is a per-lane part per k
+  // chunk c plus a wave-uniform row offset.
+  auto lfo = [&](int c) { return lr * BK + swz<BK>(lr, c) * 8; };
   if constexpr (MF16) {
     // v_mfma_f32_16x16x32_bf16: lane l supplies row (or column) l & 15 of a
     // 16-row operand block and its k values 8 (l >> 4) .. + 7 of the k-step's
@@ -266,12 +286,10 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     static_assert(TN >= TM, "the next k-step's A reads follow the first TM columns");
     constexpr int JW = TN / 2;                 // columns of the last k-step before the wait
     auto rdA = [&](const bf16* sA, int ks, int set, int i) {
-      const int row = wm * WM + i * 16 + lr, c = ks * 4 + lh;
-      fa[set][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
+      fa[set][i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WM + i * 16) * BK + lfo(ks * 4 + lh));
     };
     auto rdB = [&](const bf16* sB, int ks, int j) {
-      const int row = ncol(j) + lr, c = ks * 4 + lh;
-      fb[j] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
+      fb[j] = *reinterpret_cast<const bf16x8*>(sB + ncol(j) * BK + lfo(ks * 4 + lh));
     };
     auto mfma_col = [&](int set, int j) {
   #pragma unroll
@@ -400,11 +418,9 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       const int c = ks * 2 + lh;
       if (x == 0 || x > TN) {
         const int i = x == 0 ? 0 : x - TN;
-        const int row = wm * WM + i * 32 + lr;
-        af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
+        af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WM + i * 32) * BK + lfo(c));
       } else {
-        const int row = ncol(x - 1) + lr;
-        bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
+        bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + ncol(x - 1) * BK + lfo(c));
       }
     };
     auto mfma_pair = [&](int fs, int pr) {
@@ -1146,8 +1162,6 @@ constexpr Variant kVariants[V_COUNT] = {
     {128, 128, 2, 2, 1.08f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
     {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.45f, true},
 };
-// the 320-wide tile: no QKV or argmax epilogue, whole rounds only
-constexpr bool wide_tile(int bn) { return bn == 320; }
 // Constants fitted to a sweep of every (variant, split) plan over the
 // decode, prefill, lm_head and decode-argmax shapes of the Qwen3-0.6B / 32B
 // shards on MI355X (27 shapes; the chosen plans are within 1% of the
@@ -1202,7 +1216,7 @@ double plan_cost(const Variant& v, int64_t M, int64_t N, int64_t K, int epi, int
 }
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool consumer_sums = false,
-               double* cost_out = nullptr) {
+               double* cost_out = nullptr, bool gathered = false) {
   Plan best{V256x256, 1, K, 0, 0};
   double best_cost = 1e300;
   const int64_t kblocks = (K + 63) / 64;
@@ -1213,7 +1227,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
     for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
       if (sp > 1 && (!allow_split || !quad_cols || kblocks < 4 * sp)) break;
       if (epi == EPI_SILU_BF16 && !v.silu) continue;
-      if (wide_tile(v.bn) && (epi == EPI_QKV || epi == EPI_ARGMAX)) continue;
+      if (wide_tile(v.bn) && (epi == EPI_QKV || epi == EPI_ARGMAX || gathered)) continue;
       if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
@@ -1355,7 +1369,7 @@ bool persistent_plan(const Plan& pl, int epi, bool gathered) {
 
 Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool gathered) {
   double best_cost = 0;
-  Schedule best{make_plan(M, N, K, epi, allow_split, false, &best_cost), 0, Plan{}};
+  Schedule best{make_plan(M, N, K, epi, allow_split, false, &best_cost, gathered), 0, Plan{}};
   if (!(epi == EPI_BF16 || epi == EPI_SILU_BF16 || epi == EPI_QKV || epi == EPI_ARGMAX)) return best;
   // a row gather reads A the same way in every column slice; the schedule of
   // a gathered problem is the plain one for the argmax epilogue (whose
