@@ -752,7 +752,7 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wave_u / WGN, wn = wave_u % WGN;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t M = p.M, K = p.K;
   const int nk = (int)((K + BK - 1) / BK);
@@ -787,15 +787,14 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   constexpr int A_G = BM / (RPI * NW), B_G = BN / (RPI * NW), NV = A_G + B_G;
   const int grow = lane / KC, gpc = lane % KC;
   const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
-  uint32_t voff[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const bool isA = v < A_G;
-    const int g = wave + (isA ? v : v - A_G) * NW;
-    const bool up = !isA && EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
-    const int row = g * RPI + grow - (up ? BN / 2 : 0);
-    voff[v] = (uint32_t)(row * (isA ? lda_b : ldb_b) + (swz<BK>(row, gpc) << 4));
-  }
+  // slice offsets: a per-lane part per operand plus the slice's first row
+  // times the row pitch (wave-uniform; every slice of a wave starts on the
+  // same row modulo the swizzle's 16-row period)
+  static_assert(EPI != EPI_SILU_BF16 || (BN / 2) % 16 == 0, "gate/up halves in whole 16-row units");
+  auto b_up = [&](int g) { return EPI == EPI_SILU_BF16 && g * RPI >= BN / 2; };
+  auto src_row0 = [&](bool isA, int g) -> int { return g * RPI - (!isA && b_up(g) ? BN / 2 : 0); };
+  const uint32_t lsw = (uint32_t)(swz<BK>(((wave_u * RPI) & 15) + grow, gpc) << 4);
+  const uint32_t lane_a = (uint32_t)(grow * lda_b) + lsw, lane_b = (uint32_t)(grow * ldb_b) + lsw;
   // descriptors of the tile that the loads are filling (they run ahead of
   // the MFMAs by S - 1 blocks, so into the next tile near a tile's end)
   __amdgpu_buffer_rsrc_t ra, rg, ru;
@@ -807,21 +806,22 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     rg = make_rsrc(p.B + nrow0 * p.ldb, nrows * ldb_b);
     ru = make_rsrc(p.B + ((p.up_off ? p.up_off : p.li) + nrow0) * p.ldb, nrows * ldb_b);
   };
+  auto slice = [&](int v, bf16* st, uint32_t ko) __attribute__((always_inline)) {
+    if (v < A_G) {
+      const int g = wave_u + v * NW;
+      dma16(ra, lane_a + (uint32_t)(src_row0(true, g) * lda_b) + ko, st + g * RPI * BK);
+    } else {
+      const int g = wave_u + (v - A_G) * NW;
+      dma16(b_up(g) ? ru : rg, lane_b + (uint32_t)(src_row0(false, g) * ldb_b) + ko, st + BM * BK + g * RPI * BK);
+    }
+  };
   int dj = 0, dkb = 0;                    // tile and K block of the next load
   auto dma_next = [&](int buf) __attribute__((always_inline)) {
     if (dkb == 0) set_dma_tile(dj);
     bf16* st = smem + buf * STAGE;
     const uint32_t ko = (uint32_t)dkb * (BK * 2);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      if (v < A_G) {
-        dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
-      } else {
-        const int g = wave_u + (v - A_G) * NW;
-        const bool up = EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
-        dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
-      }
-    }
+    for (int v = 0; v < NV; ++v) slice(v, st, ko);
     if (++dkb == nk) {
       dkb = 0;
       ++dj;
@@ -829,15 +829,7 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   };
   // one slice of the next load (issued inside the fenced MFMA stream)
   auto dma_slice = [&](int v, int buf) __attribute__((always_inline)) {
-    bf16* st = smem + buf * STAGE;
-    const uint32_t ko = (uint32_t)dkb * (BK * 2);
-    if (v < A_G) {
-      dma16(ra, voff[v] + ko, st + (wave_u + v * NW) * RPI * BK);
-    } else {
-      const int g = wave_u + (v - A_G) * NW;
-      const bool up = EPI == EPI_SILU_BF16 && g * RPI >= BN / 2;
-      dma16(up ? ru : rg, voff[v] + ko, st + BM * BK + g * RPI * BK);
-    }
+    slice(v, smem + buf * STAGE, (uint32_t)dkb * (BK * 2));
   };
   auto zero_tail = [&](int buf) __attribute__((always_inline)) {
     bf16* st = smem + buf * STAGE;
@@ -871,14 +863,14 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   constexpr int H1 = NPAIR / 2;
   constexpr int RDP2 = (NF + (NPAIR - H1) - 1) / (NPAIR - H1);
   auto read_frag = [&](const bf16* sA, const bf16* sB, int ks, int fs, int x) __attribute__((always_inline)) {
-    const int c = ks * 2 + lh;
+    // lane row lr plus a multiple of 16: a per-lane part per k chunk and a
+    // wave-uniform row offset
+    const int c = ks * 2 + lh, lo = lr * BK + swz<BK>(lr, c) * 8;
     if (x == 0 || x > TN) {
       const int i = x == 0 ? 0 : x - TN;
-      const int row = wm * WM + i * 32 + lr;
-      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + row * BK + swz<BK>(row, c) * 8);
+      af[fs][i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WM + i * 32) * BK + lo);
     } else {
-      const int row = ncol(x - 1) + lr;
-      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + row * BK + swz<BK>(row, c) * 8);
+      bfr[fs][x - 1] = *reinterpret_cast<const bf16x8*>(sB + ncol(x - 1) * BK + lo);
     }
   };
   auto mfma_pair = [&](int fs, int pr) __attribute__((always_inline)) {
@@ -1025,15 +1017,15 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     if (tile_end) {
       epilogue(cj);
       zero_acc();
-      ckb = 0;
-      ++cj;
       if constexpr (NEXT) {
 #pragma unroll
         for (int x = 0; x < NF; ++x) read_frag(nA, nB, 0, 0, x);
       }
-    } else {
-      ++ckb;
     }
+    // both counters stored on every path (increments of one or the other
+    // became a select of their addresses, which kept them in scratch)
+    cj += tile_end ? 1 : 0;
+    ckb = tile_end ? 0 : ckb + 1;
   };
 
   if (total > 0) {
