@@ -1138,21 +1138,23 @@ struct Variant {
   float t_kb_us;       // time per 64-wide K block per resident round at full load
   bool silu;           // the tile can hold gate/up pairs
 };
-// V256x320: 256 x 320 tiles (waves of 64 x 160) for the row-parallel
-// projections, whose N = 5120 is 16 such tiles: at 4096 rows that is one
-// round of 256 tiles, where 256-wide tiles need 1.25 rounds (or a second
-// launch for the last 1024 columns); likewise the 32B gate_up (12800 SiLU
-// outputs, 160 per tile) is five whole rounds at 4096 rows, where 256-wide
-// tiles need 6.25.  Bf16, fp32 and SiLU outputs (a 320-wide tile does not
-// hold whole 128-column heads), and only grids of whole rounds: other long
-// grids keep the 256-wide tiles and the persistent kernel.
+// V256x320: 256 x 320 tiles (waves of 64 x 160).  The row-parallel
+// projections' N = 5120 is 16 such tiles: at 4096 rows that is one round of
+// 256 tiles, where 256-wide tiles need 1.25 rounds (or a second launch for
+// the last 1024 columns); the 32B gate_up (12800 SiLU outputs, 160 per
+// tile) is five whole rounds at 4096 rows, where 256-wide tiles need 6.25.
+// On long grids at K = 5120 it also beats 256-wide tiles per flop (the
+// 32B lm_head 8-10%, at 2048 and 4096 rows); its time per K block is the
+// measured one, below the 1.25 x 256 x 256 one its area would give.  Bf16,
+// fp32 and SiLU outputs (a 320-wide tile does not hold whole 128-column
+// heads); grids beyond one round only unsplit and at K >= 2048.
 enum VariantId {
   V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V256x320, V_COUNT
 };
 constexpr Variant kVariants[V_COUNT] = {
     {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.59f, true},
     {128, 128, 2, 2, 1.08f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
-    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.45f, true},
+    {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.29f, true},
 };
 // Constants fitted to a sweep of every (variant, split) plan over the
 // decode, prefill, lm_head and decode-argmax shapes of the Qwen3-0.6B / 32B
@@ -1224,7 +1226,9 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
       const double c = plan_cost(v, M, N, K, epi, sp, &tm, &tn, consumer_sums) * (sp > 1 ? 1.05 : 1.0);
-      if (wide_tile(v.bn) && tm * tn * sp > kCUs && (sp > 1 || (tm * tn) % kCUs != 0)) continue;
+      // beyond one round only unsplit and with at least 32 K blocks: on the
+      // 0.6B lm_head (K = 1024) the persistent kernel measured 2-3% faster
+      if (wide_tile(v.bn) && tm * tn * sp > kCUs && (sp > 1 || K < 32 * 64)) continue;
       if (c < best_cost * 0.999) {
         best_cost = c;
         const int64_t kps = sp == 1 ? K : ((kblocks + sp - 1) / sp) * 64;

@@ -233,12 +233,13 @@ def test_embed_vocab_bit_exact_and_vocab_sum(case):
 
 # ------------------------------------------------------------------ lm_head
 
-@pytest.mark.parametrize("case", ["w3", "w4-32b-tp2", "w5-32b-tp16", "mid", "many-ragged"])
+@pytest.mark.parametrize("case", ["w3", "w4-32b-tp2", "w5-32b-tp16", "mid", "many-ragged", "persistent-ragged"])
 def test_lm_head(case):
     """Logits of a vocab shard.  w3 and the 32B cases are the bench's lm_head
     shapes at full size (4096 rows at tp=2 and 1024 rows at tp=16 of the 32B
-    hidden size 5120: the persistent kernel over 80 K blocks), sampled rows
-    against the oracle."""
+    hidden size 5120), sampled rows against the oracle; the ragged cases also
+    check from the kernel marks which GEMM kernel ran."""
+    kernel = None
     if case == "w3":
         w = synth.WORKLOADS[3]
         V, H, n, M = w["vocab"], w["hidden"], w["tp"], w["n_ids"]
@@ -255,14 +256,25 @@ def test_lm_head(case):
         rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(wid).integers(0, M, 8)]))
         ranks = [0]
     elif case == "many-ragged":
-        # over eight rounds of 256 x 256 tiles (the persistent kernel), with
-        # ragged M, N and K tails
-        V, H, n, M = 116400, 1000, 2, 2100
+        # 11.4 rounds of 256 x 320 tiles (33 K blocks), with ragged M, N and
+        # K tails
+        V, H, n, M = 116400, 2104, 2, 3996
         E = synth.embedding(12, V, H)
         x = synth.activations(12, M, H)
-        rows = np.unique(np.concatenate([[0, 255, 256, 1279, 1280, 2047, 2048, M - 1],
+        rows = np.unique(np.concatenate([[0, 255, 256, 1279, 1280, 2047, 2048, 3839, 3840, M - 1],
                                          np.random.default_rng(12).integers(0, M, 8)]))
         ranks = [1]
+        kernel = "gemm_tile<256,320,2>/bf16"
+    elif case == "persistent-ragged":
+        # eight rounds of 256 x 256 tiles (the persistent kernel), with ragged
+        # M, N and K tails
+        V, H, n, M = 65462, 1000, 2, 3996
+        E = synth.embedding(13, V, H)
+        x = synth.activations(13, M, H)
+        rows = np.unique(np.concatenate([[0, 255, 256, 2047, 2048, 3839, 3840, M - 1],
+                                         np.random.default_rng(13).integers(0, M, 8)]))
+        ranks = [0]
+        kernel = "gemm_persist<256,256,2>/bf16"
     else:
         V, H, n, M = 777, 520, 2, 300
         E = synth.embedding(11, V, H)
@@ -276,8 +288,16 @@ def test_lm_head(case):
         shard = torch.empty(L.vocab_end - L.vocab_start, H, dtype=torch.bfloat16, device=DEV)
         tp.tp_shard_weights(c, tp.TP_W_VOCAB, Eg, shard)
         logits = torch.empty(M, L.vocab_end - L.vocab_start, dtype=torch.bfloat16, device=DEV)
-        tp.tp_lm_head(c, xg, M, shard, logits)
-        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        tp.tp_kernel_marks(ev)
+        try:
+            tp.tp_lm_head(c, xg, M, shard, logits)
+            torch.cuda.synchronize()
+            names = tp.tp_kernel_mark_names()
+        finally:
+            tp.tp_kernel_marks([])
+        if kernel:
+            assert any(nm.startswith(kernel) for nm in names), (case, names)
         ref = O.lm_head(synth.to_f64(x)[rows], synth.to_f64(E[L.vocab_start:L.vocab_end]))
         err = relerr(f64(logits)[rows], ref)
         assert err <= TOL_BF16, (case, r, err)
