@@ -66,13 +66,16 @@ __device__ __forceinline__ void wait_vm() {
 }
 // ---- merged QKV finish: QK-norm and RoPE per (row, head) in qkv_finish.h;
 // here the store of q, or the append of k / v to the caches.
-// x[0..3] hold d = 4j .. 4j+3 of (row m, head h), x[4..7] hold d + 64
-__device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
-                                           const RopeCoef& rc) {
+// x[0..3] hold d = 4j .. 4j+3 of (row m = b T + t, head h), x[4..7] hold d + 64;
+// nw: the lane's weights of that head's norm (q or k)
+__device__ __forceinline__ const bf16* norm_of(const QkvArgs& a, int h) {
+  return h + a.head0 < a.lq ? a.q_norm_w : a.k_norm_w;
+}
+__device__ __forceinline__ void qkv_finish_at(const QkvArgs& a, float (&x)[8], int64_t m, int b, int t, int h, int j,
+                                              const RopeCoef& rc, const NormW& nw) {
   h += a.head0;
-  const int b = (int)(m / a.T), t = (int)(m - (int64_t)b * a.T);
   const int pos = a.past + t;
-  if (h < a.lq + a.lkv) qk_norm_rope(x, h < a.lq ? a.q_norm_w : a.k_norm_w, pos, j, rc, a.eps);
+  if (h < a.lq + a.lkv) qk_norm_rope(x, nw, pos, rc, a.eps);
   bf16* dst;
   if (h < a.lq)
     dst = a.q_out + m * ((int64_t)a.lq * 128) + (int64_t)h * 128;
@@ -82,8 +85,13 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
     dst = a.v_cache + (((int64_t)b * a.lkv + (h - a.lq - a.lkv)) * a.S_max + pos) * 128;
   store_head_lanes(dst, x, j);
 }
-// the 320-wide tile: no QKV or argmax epilogue, no row gather, whole rounds
-// of tiles only
+__device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
+                                           const RopeCoef& rc) {
+  const int b = (int)(m / a.T);
+  qkv_finish_at(a, x, m, b, (int)(m - (int64_t)b * a.T), h, j, rc, norm_w(norm_of(a, h), j));
+}
+// the 320-wide tile: no QKV or argmax epilogue, no row gather; beyond one
+// round only unsplit and at K >= 2048
 constexpr bool wide_tile(int bn) { return bn == 320; }
 // the fp32 tile of a QKV epilogue fits the LDS ring and covers whole heads
 // (the epilogue stages the tile 128 columns -- one head -- at a time)
@@ -597,6 +605,10 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     const RopeCoef rc = rope_coef(p.qkv.theta, j16);
     constexpr int HPT = BN / 128;                      // heads per tile
     const int heads = (int)(p.N / 128);
+    // sequence and position of this thread's first row (one 64-bit
+    // division); the rows after it step by NT / 16 and wrap at T
+    const int64_t mf = m0 + (tid >> 4);
+    const int bf0 = (int)(mf / p.qkv.T), tf0 = (int)(mf - (int64_t)bf0 * p.qkv.T);
 #pragma unroll
     for (int hh = 0; hh < HPT; ++hh) {
       __syncthreads();   // the ring (first head) or the previous head's staging is no longer read
@@ -612,14 +624,23 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
       }
       __syncthreads();
       const int h = tn * HPT + hh;
+      const NormW nw = norm_w(norm_of(p.qkv, h), j16);
+      int b = bf0, t = tf0;
       for (int r = tid >> 4; r < BM; r += NT / 16) {
         const int64_t m = m0 + r;
-        if (m >= M || h >= heads) continue;
-        // four consecutive columns are one 16-byte group of the staged tile
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + st_off(r, 4 * j16));
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + st_off(r, 64 + 4 * j16));
-        float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        qkv_finish(p.qkv, x, m, h, j16, rc);
+        if (m < M && h < heads) {
+          // four consecutive columns are one 16-byte group of the staged tile
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + st_off(r, 4 * j16));
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + st_off(r, 64 + 4 * j16));
+          float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          qkv_finish_at(p.qkv, x, m, b, t, h, j16, rc, nw);
+        }
+        t += NT / 16;
+        if (t >= p.qkv.T) {
+          const int q = t / p.qkv.T;
+          b += q;
+          t -= q * p.qkv.T;
+        }
       }
     }
     return;

@@ -41,21 +41,32 @@ __device__ __forceinline__ void rope_sincos(int pos, float hi, float lo, float& 
   sn = __builtin_amdgcn_sinf(rev);
   cs = __builtin_amdgcn_cosf(rev);
 }
+// the lane's norm weights, d = 4j .. 4j+3 and d + 64, as floats
+struct NormW {
+  float v[8];
+};
+__device__ __forceinline__ NormW norm_w(const bf16* w, int j) {
+  const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(w + 4 * j), w1 = *reinterpret_cast<const bf16x4*>(w + 64 + 4 * j);
+  NormW r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r.v[e] = bf2f(w0[e]);
+    r.v[4 + e] = bf2f(w1[e]);
+  }
+  return r;
+}
 // x *= rsqrt(mean(x^2) + eps) * w over the head's 128 values (16 lanes),
-// then the rotation at position pos
-__device__ __forceinline__ void qk_norm_rope(float (&x)[8], const bf16* w, int pos, int j, const RopeCoef& rc,
-                                             float eps) {
+// then the rotation at position pos.  The reciprocal square root is the
+// hardware one (about 1 ulp of fp32, far below the bf16 rounding of the
+// result).
+__device__ __forceinline__ void qk_norm_rope(float (&x)[8], const NormW& w, int pos, const RopeCoef& rc, float eps) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
   ss = row_sum16(ss);
-  const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
-  const bf16x4 w0 = *reinterpret_cast<const bf16x4*>(w + 4 * j), w1 = *reinterpret_cast<const bf16x4*>(w + 64 + 4 * j);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / 128.0f) + eps);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] *= inv * bf2f(w0[e]);
-    x[4 + e] *= inv * bf2f(w1[e]);
-  }
+  for (int e = 0; e < 8; ++e) x[e] *= inv * w.v[e];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float sn, cs;
@@ -64,6 +75,10 @@ __device__ __forceinline__ void qk_norm_rope(float (&x)[8], const bf16* w, int p
     x[e] = x1 * cs - x2 * sn;
     x[4 + e] = x2 * cs + x1 * sn;
   }
+}
+__device__ __forceinline__ void qk_norm_rope(float (&x)[8], const bf16* w, int pos, int j, const RopeCoef& rc,
+                                             float eps) {
+  qk_norm_rope(x, norm_w(w, j), pos, rc, eps);
 }
 // the lane's eight values of a 128-wide head row at dst, as bf16
 __device__ __forceinline__ void store_head_lanes(bf16* dst, const float (&x)[8], int j) {
