@@ -87,7 +87,9 @@ __device__ __forceinline__ void qkv_finish_at(const QkvArgs& a, float (&x)[8], i
 }
 __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int64_t m, int h, int j,
                                            const RopeCoef& rc) {
-  const int b = (int)(m / a.T);
+  // (a 32-bit division where the row index allows: the 64-bit one is a
+  // long expansion)
+  const int b = m < 0x7fffffff ? (int)((uint32_t)m / (uint32_t)a.T) : (int)(m / a.T);
   qkv_finish_at(a, x, m, b, (int)(m - (int64_t)b * a.T), h, j, rc, norm_w(norm_of(a, h), j));
 }
 // the 320-wide tile: no QKV or argmax epilogue, no row gather; beyond one
@@ -1116,8 +1118,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv(const float* __restrict
   const int heads = (int)(N / 128);
   const int j = threadIdx.x & 15;
   const RopeCoef rc = rope_coef(a.theta, j);
+  const bool narrow = M * heads < 0x7fffffff;   // 32-bit unit indices
   for (int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; u < M * heads; u += (int64_t)gridDim.x * 16) {
-    const int64_t m = u / heads;
+    const int64_t m = narrow ? (int64_t)((uint32_t)u / (uint32_t)heads) : u / heads;
     const int h = (int)(u - m * heads);
     f32x4 v0[kMaxSplits], v1[kMaxSplits];
 #pragma unroll
