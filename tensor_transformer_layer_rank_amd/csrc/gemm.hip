@@ -714,6 +714,22 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
   __builtin_amdgcn_wave_barrier();
   const int64_t row0 = m0 + wm * WM + ps * PR;
+  // a pass wholly inside the output (the common case): no per-chunk bounds,
+  // 32-bit offsets from the pass's first element (rows below 2^22 elements)
+  if (vec && row0 + PR <= M && col0 + OC <= ncols && p.ldc < (int64_t(1) << 22)) {
+    bf16* cb = C + row0 * p.ldc + col0;
+    const uint32_t ldc = (uint32_t)p.ldc;
+#pragma unroll 4
+    for (int q = lane; q < PR * OCH; q += 64) {
+      const int r = q / OCH, c = q % OCH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * OC + (och(r, c) << 3));
+      // streaming store: the output is not read again by this kernel, and
+      // allocating it in L2 would evict the A/B panels that other tiles
+      // still read (the lm_head writes four times the bytes it reads)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(cb + ((uint32_t)r * ldc + (uint32_t)(c * 8))));
+    }
+    continue;
+  }
 #pragma unroll 4
   for (int q = lane; q < PR * OCH; q += 64) {
     const int r = q / OCH, c = q % OCH;
@@ -721,9 +737,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
     if (gm >= M || gc >= ncols) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(so + r * OC + (och(r, c) << 3));
     if (vec && gc + 8 <= ncols) {
-      // streaming store: the output is not read again by this kernel, and
-      // allocating it in L2 would evict the A/B panels that other tiles
-      // still read (the lm_head writes four times the bytes it reads)
+      // streaming store (as above)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + gm * p.ldc + gc));
     } else {
 #pragma unroll
