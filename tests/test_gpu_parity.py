@@ -433,6 +433,34 @@ def test_mlp_wide_tile_silu_ragged():
     assert relerr(f64(part), p_ref) <= TOL_BF16
 
 
+def test_mlp_wide_tile_silu_two_rounds_sampled():
+    """The gate_up + SiLU GEMM on two rounds of 320-row weight tiles (512
+    tiles; 33 K blocks, the last ragged), then a down projection on 256 x 128
+    tiles with a split-K tail: sampled rows against the oracle, element by
+    element.  The kernel marks confirm the tile shape ran."""
+    w = dict(hidden=2104, intermediate=10000, n_q_heads=2, n_kv_heads=2, head_dim=128, vocab=0, tp=2)
+    wid, M = 122, 3900
+    W = synth.full_weights(wid, w)
+    rk = Rank(w, 0, {k: v.to(DEV) for k, v in W.items()})
+    oc = ocfg(w, 0)
+    gu = O.merge_gate_up(shard64(oc, O.W_GATE, W["gate"]), shard64(oc, O.W_UP, W["up"]))
+    down = shard64(oc, O.W_DOWN, W["down"])
+    x = synth.activations(wid, M, w["hidden"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    tp.tp_kernel_marks(ev)
+    try:
+        h, part = run_mlp(rk, x.to(DEV), M)
+        torch.cuda.synchronize()
+        names = tp.tp_kernel_mark_names()
+    finally:
+        tp.tp_kernel_marks([])
+    assert any(n.startswith("gemm_tile<256,320,2>/silu[3900x10000x2104]") for n in names), names
+    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, M - 1], np.random.default_rng(M).integers(0, M, 10)]))
+    h_ref, p_ref = O.mlp(oc, synth.to_f64(x)[rows], gu, down)
+    assert relerr(f64(h)[rows], h_ref) <= TOL_BF16
+    assert relerr(f64(part)[rows], p_ref) <= TOL_BF16
+
+
 # ------------------------------------------------------------------ attention
 
 def make_cache(w, wid, rk, B, S_max, past, n_global_kv):
