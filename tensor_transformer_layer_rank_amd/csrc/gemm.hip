@@ -92,6 +92,8 @@ __device__ __forceinline__ void qkv_finish(const QkvArgs& a, float (&x)[8], int6
   const int b = m < 0x7fffffff ? (int)((uint32_t)m / (uint32_t)a.T) : (int)(m / a.T);
   qkv_finish_at(a, x, m, b, (int)(m - (int64_t)b * a.T), h, j, rc, norm_w(norm_of(a, h), j));
 }
+// problems of at most this many rows run the small tiles in the 16x16 form
+constexpr int64_t kMf16RowsPlan = 256;
 // the 320-wide tile: no QKV or argmax epilogue, no row gather; beyond one
 // round only unsplit and at K >= 2048
 constexpr bool wide_tile(int bn) { return bn == 320; }
@@ -1187,12 +1189,14 @@ struct Variant {
 // fp32 and SiLU outputs (a 320-wide tile does not hold whole 128-column
 // heads); grids beyond one round only unsplit and at K >= 2048.
 enum VariantId {
-  V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V256x320, V_COUNT
+  V256x256, V256x128, V128x128_4, V128x128_2, V128x64_3, V128x64_6, V64x128_3, V64x64_8, V256x320, V128x192,
+  V_COUNT
 };
 constexpr Variant kVariants[V_COUNT] = {
     {256, 256, 2, 1, 1.96f, true}, {256, 128, 3, 1, 0.98f, true}, {128, 128, 4, 1, 0.59f, true},
     {128, 128, 2, 2, 1.08f, true}, {128, 64, 3, 2, 0.73f, true},  {128, 64, 6, 1, 0.45f, true},
     {64, 128, 3, 2, 0.75f, true},  {64, 64, 8, 1, 0.30f, false},  {256, 320, 2, 1, 2.29f, true},
+    {128, 192, 4, 1, 0.885f, true},
 };
 // Constants fitted to a sweep of every (variant, split) plan over the
 // decode, prefill, lm_head and decode-argmax shapes of the Qwen3-0.6B / 32B
@@ -1260,6 +1264,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int epi, bool allow_split, bool 
       if (sp > 1 && (!allow_split || !quad_cols || kblocks < 4 * sp)) break;
       if (epi == EPI_SILU_BF16 && !v.silu) continue;
       if (wide_tile(v.bn) && (epi == EPI_QKV || epi == EPI_ARGMAX || gathered)) continue;
+      if (v.bn == 192 && (epi != EPI_SILU_BF16 || M <= kMf16RowsPlan || sp > 1)) continue;
       if (epi == EPI_QKV && sp == 1 && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
       int64_t tm, tn;
       // a split must win clearly: its partials also cost workspace
@@ -1420,7 +1425,7 @@ Schedule make_schedule(int64_t M, int64_t N, int64_t K, int epi, bool allow_spli
   for (int vi = 0; vi < V_COUNT; ++vi) {
     const Variant& v = kVariants[vi];
     if (epi == EPI_SILU_BF16 && !v.silu) continue;
-    if (wide_tile(v.bn)) continue;   // whole rounds only: nothing to split off
+    if (wide_tile(v.bn) || v.bn == 192) continue;   // single-plan tiles: nothing to split off
     if (epi == EPI_QKV && !qkv_tile_ok(v.bm, v.bn, v.stages)) continue;
     int64_t tm, tn;
     plan_cost(v, M, N, K, epi, 1, &tm, &tn);
@@ -1499,7 +1504,7 @@ namespace {
 
 // Problems of at most this many rows (decode batches: the weight stream)
 // run the small tiles in the 16x16x32 form.
-constexpr int64_t kMf16Rows = 256;
+constexpr int64_t kMf16Rows = kMf16RowsPlan;
 template <int BM, int BN, int WGM, int WGN, int S>
 hipError_t launch_rows(const GemmProblem& p, int epi, const Plan& pl, void* scratch, hipStream_t s, bool finish) {
   if (p.M <= kMf16Rows) return launch_tile<BM, BN, WGM, WGN, S, true>(p, epi, pl, scratch, s, finish);
@@ -1517,6 +1522,7 @@ hipError_t launch_plan(const GemmProblem& p, int epi, const Plan& pl, void* scra
     case V128x64_6: return launch_rows<128, 64, 4, 1, 6>(p, epi, pl, scratch, s, finish);
     case V64x128_3: return launch_rows<64, 128, 2, 2, 3>(p, epi, pl, scratch, s, finish);
     case V256x320: return launch_tile<256, 320, 4, 2, 2>(p, epi, pl, scratch, s, finish);
+    case V128x192: return launch_tile<128, 192, 4, 2, 4>(p, epi, pl, scratch, s, finish);
     default: return launch_rows<64, 64, 2, 2, 8>(p, epi, pl, scratch, s, finish);
   }
 }
@@ -1564,7 +1570,8 @@ hipError_t gemm_qkv(const GemmProblem& p, void* scratch, size_t scratch_bytes, b
     case V128x64_3: return launch_rows<128, 64, 4, 1, 3>(p, EPI_QKV, pl, scratch, s, !split);
     case V128x64_6: return launch_rows<128, 64, 4, 1, 6>(p, EPI_QKV, pl, scratch, s, !split);
     case V64x128_3: return launch_rows<64, 128, 2, 2, 3>(p, EPI_QKV, pl, scratch, s, !split);
-    case V256x320: return hipErrorInvalidValue;   // never planned for QKV
+    case V256x320:   // never planned for QKV
+    case V128x192: return hipErrorInvalidValue;
     default: return launch_rows<64, 64, 2, 2, 8>(p, EPI_QKV, pl, scratch, s, !split);
   }
 }
