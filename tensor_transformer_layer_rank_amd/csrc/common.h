@@ -109,6 +109,12 @@ __device__ __forceinline__ float wave_sum64(float v) {
 }
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // RNE (v_cvt_pk_bf16_f32)
 // two floats to packed bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32, RNE
+// silu(g) * u ("Implementation", TPMLP: silu(gate) times up), with the
+// hardware reciprocal (about 1 ulp of fp32) in place of an IEEE division,
+// whose expansion dominated the SiLU epilogues
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -704,7 +704,7 @@ void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int64_t k_per_split) {
           const int e = 4 * g4 + q;
           if (EPI == EPI_SILU_BF16) {
             const float g = acc[i][j][e], u = SI ? acc[i][j][e + 8] : acc[i][j + TN / 2][e];
-            v[q] = g / (1.f + __expf(-g)) * u;
+            v[q] = silu_mul(g, u);
           } else {
             v[q] = acc[i][j][e];
           }
@@ -954,7 +954,7 @@ void gemm_persist_kernel(GemmProblem p, int tiles_m, int tiles_n) {
               const int e = 4 * g4 + q;
               if (EPI == EPI_SILU_BF16) {
                 const float g = acc[i][ps * 2 + jj][e], u = acc[i][ps * 2 + jj + TN / 2][e];
-                v[q] = g / (1.f + __expf(-g)) * u;
+                v[q] = silu_mul(g, u);
               } else {
                 v[q] = acc[i][ps * 2 + jj][e];
               }
@@ -1118,7 +1118,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (EPI == EPI_SILU_BF16)
-        static_cast<bf16*>(out)[m * ldc + n + e] = f2bf(sg[e] / (1.f + __expf(-sg[e])) * su[e]);
+        static_cast<bf16*>(out)[m * ldc + n + e] = f2bf(silu_mul(sg[e], su[e]));
       else if (EPI == EPI_BF16)
         static_cast<bf16*>(out)[m * ldc + n + e] = f2bf(sg[e]);
       else
